@@ -1,0 +1,335 @@
+/*
+ * Plain CPU oracle for the tiled dense GEMM.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The GPU product path never calls it, and it shares
+ * no code, header or table with the GPU path.
+ *
+ * What is computed (the definition, not a fast method):
+ *
+ *   NT:     C[m][n] = R_out( sum_{k=0}^{K-1} A[m][k] * B[n][k] )
+ *           A is M x K, B is N x K, both row-major (TileLang SM100 README,
+ *           "Code Example": A (M,K), B (N,K), gemm with trans_B=True).
+ *   NN:     C[m][n] = R_out( sum_k A[m][k] * B[k][n] )
+ *           B is K x N row-major (velog "tilelang", 1.1 Front-End DSL:
+ *           B: T.Tensor((K, N)) and T.gemm(A_shared, B_shared, C_local)).
+ *   MXFP8:  C[m][n] = R_bf16( sum_k (q(A[m][k]) * 2^(EA[m][k/128]-127))
+ *                                 * (q(B[n][k]) * 2^(EB[n][k/128]-127)) )
+ *           one e8m0 scale per row per 128 K elements for each operand
+ *           (Blackwell TCGEN05 GEMM tutorial, "进阶" (Advanced):
+ *           gemm_blockscaled with sf_a_granularity_k = sf_b_granularity_k = 128).
+ *
+ * Products and the running sum are IEEE binary64, summed in sequential k
+ * order k = 0..K-1 with one accumulator per output, and R_out is a single
+ * round-to-nearest-even from binary64 to the output type.  The pages' own
+ * check rounds an fp32 matmul to the output type once (SM100 README,
+ * "Compilation and Usage": ref_c = (a.float @ b.T.float).to(bfloat16));
+ * binary64 is the stricter reading.
+ *
+ * The outer loop over rows m is split across OpenMP threads.  That changes
+ * no arithmetic: every output is still one sequential k-ordered sum.
+ *
+ * Build: gcc -O2 -fopenmp -fPIC -shared (no -ffast-math: the k order of the
+ * sum must not be changed by the compiler).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Decoders: bit patterns -> binary64 (exact).                               */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 is the upper half of an IEEE binary32 word. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);               /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);   /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 fraction bits,
+ * no infinities, S.1111.111 is NaN, largest finite 448. */
+double oracle_e4m3fn_to_f64(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 3) & 0xf;
+    int f = b & 0x7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);                /* f/8 * 2^(1-7) */
+    else
+        v = ldexp((double)(8 + f), e - 10);      /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* OCP E8M0 scale: an unsigned biased exponent, value 2^(E-127); 0xFF is NaN. */
+double oracle_e8m0_to_f64(uint8_t e)
+{
+    if (e == 0xff)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encoders: binary64 -> nearest representable, ties to even, one rounding.  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Round |x| to a floating-point grid with `p` significant bits, minimum
+ * normal exponent `emin` (value 2^emin) and subnormals below it.  Returns the
+ * rounded magnitude as a binary64 (exact: p <= 11 here, well inside 53 bits).
+ *
+ * The quantum (spacing of the grid at |x|) is 2^(floor(log2|x|) - (p-1)) in
+ * the normal range and 2^(emin - (p-1)) below it.  |x| / quantum is exact
+ * (a power-of-two scaling), and nearbyint() in the default rounding mode
+ * rounds halfway cases to the even integer.
+ */
+static double round_to_grid(double ax, int p, int emin)
+{
+    int e2;
+    (void)frexp(ax, &e2);            /* ax = f * 2^e2, f in [0.5, 1) */
+    int ex = e2 - 1;                 /* floor(log2(ax)) for ax > 0 */
+    if (ex < emin)
+        ex = emin;
+    double quantum = ldexp(1.0, ex - (p - 1));
+    return nearbyint(ax / quantum) * quantum;
+}
+
+/* binary64 -> bfloat16 (8 significant bits, exponent range of binary32). */
+uint16_t oracle_f64_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0)
+        return sign;
+    if (isinf(ax))
+        return sign | 0x7f80;
+    double r = round_to_grid(ax, 8, -126);
+    if (r >= ldexp(1.0, 128))        /* rounded past the largest finite */
+        return sign | 0x7f80;
+    /* r is a bfloat16 value, hence exactly a binary32 value. */
+    float f = (float)r;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* binary64 -> IEEE binary16 (11 significant bits, emin = -14). */
+uint16_t oracle_f64_to_f16(double x)
+{
+    if (isnan(x))
+        return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0)
+        return sign;
+    if (isinf(ax))
+        return sign | 0x7c00;
+    double r = round_to_grid(ax, 11, -14);
+    if (r >= 65536.0)                /* largest finite is 65504 */
+        return sign | 0x7c00;
+    if (r < ldexp(1.0, -14))         /* subnormal: r = f * 2^-24 */
+        return sign | (uint16_t)(r * 16777216.0);
+    int e2;
+    double fr = frexp(r, &e2);       /* r = fr * 2^e2, fr in [0.5, 1) */
+    int ex = e2 - 1;                 /* r = (1 + f/1024) * 2^ex */
+    uint16_t f = (uint16_t)(fr * 2048.0 - 1024.0);
+    return sign | (uint16_t)((ex + 15) << 10) | f;
+}
+
+/* Elementwise array forms, for the tests. */
+void oracle_decode_bf16(int64_t n, const uint16_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f64(in[i]);
+}
+void oracle_decode_f16(int64_t n, const uint16_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(in[i]);
+}
+void oracle_decode_e4m3fn(int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3fn_to_f64(in[i]);
+}
+void oracle_decode_e8m0(int64_t n, const uint8_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e8m0_to_f64(in[i]);
+}
+void oracle_encode_bf16(int64_t n, const double *in, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16(in[i]);
+}
+void oracle_encode_f16(int64_t n, const double *in, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The GEMMs.                                                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Every GEMM below writes, for each output, the binary64 sum (out64, may be
+ * NULL) and its single rounding to the output type (out, may be NULL).
+ */
+
+/* NT, bf16 in, bf16 out:  C = A . B^T  with A (M,K), B (N,K). */
+void oracle_gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
+                         const uint16_t *A, const uint16_t *B,
+                         uint16_t *C, double *C64)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += oracle_bf16_to_f64(A[m * K + k]) *
+                       oracle_bf16_to_f64(B[n * K + k]);
+            if (C64) C64[m * N + n] = acc;
+            if (C) C[m * N + n] = oracle_f64_to_bf16(acc);
+        }
+    }
+}
+
+/* NN, fp16 in, fp16 out:  C = A . B  with A (M,K), B (K,N). */
+void oracle_gemm_f16_nn(int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, const uint16_t *B,
+                        uint16_t *C, double *C64)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += oracle_f16_to_f64(A[m * K + k]) *
+                       oracle_f16_to_f64(B[k * N + n]);
+            if (C64) C64[m * N + n] = acc;
+            if (C) C[m * N + n] = oracle_f64_to_f16(acc);
+        }
+    }
+}
+
+/* Block-scaled FP8 NT, bf16 out.  qA (M,K) and qB (N,K) are e4m3fn bytes;
+ * sA (M, ceil(K/128)) and sB (N, ceil(K/128)) are e8m0 bytes, row-major. */
+void oracle_gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K,
+                          const uint8_t *qA, const uint8_t *qB,
+                          const uint8_t *sA, const uint8_t *sB,
+                          uint16_t *C, double *C64)
+{
+    const int64_t KB = (K + 127) / 128;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = oracle_e4m3fn_to_f64(qA[m * K + k]) *
+                           oracle_e8m0_to_f64(sA[m * KB + k / 128]);
+                double b = oracle_e4m3fn_to_f64(qB[n * K + k]) *
+                           oracle_e8m0_to_f64(sB[n * KB + k / 128]);
+                acc += a * b;
+            }
+            if (C64) C64[m * N + n] = acc;
+            if (C) C[m * N + n] = oracle_f64_to_bf16(acc);
+        }
+    }
+}
+
+/*
+ * Sampled forms: the same sums, for a list of P output positions
+ * (rows[p], cols[p]) only, so that full-size problems can be checked
+ * one output at a time.  out[p] / out64[p] receive C[rows[p]][cols[p]].
+ */
+void oracle_gemm_bf16_nt_at(int64_t M, int64_t N, int64_t K,
+                            const uint16_t *A, const uint16_t *B,
+                            int64_t P, const int64_t *rows, const int64_t *cols,
+                            uint16_t *out, double *out64)
+{
+    (void)M; (void)N;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = rows[p], n = cols[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += oracle_bf16_to_f64(A[m * K + k]) *
+                   oracle_bf16_to_f64(B[n * K + k]);
+        if (out64) out64[p] = acc;
+        if (out) out[p] = oracle_f64_to_bf16(acc);
+    }
+}
+
+void oracle_gemm_f16_nn_at(int64_t M, int64_t N, int64_t K,
+                           const uint16_t *A, const uint16_t *B,
+                           int64_t P, const int64_t *rows, const int64_t *cols,
+                           uint16_t *out, double *out64)
+{
+    (void)M;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = rows[p], n = cols[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += oracle_f16_to_f64(A[m * K + k]) *
+                   oracle_f16_to_f64(B[k * N + n]);
+        if (out64) out64[p] = acc;
+        if (out) out[p] = oracle_f64_to_f16(acc);
+    }
+}
+
+void oracle_gemm_mxfp8_nt_at(int64_t M, int64_t N, int64_t K,
+                             const uint8_t *qA, const uint8_t *qB,
+                             const uint8_t *sA, const uint8_t *sB,
+                             int64_t P, const int64_t *rows, const int64_t *cols,
+                             uint16_t *out, double *out64)
+{
+    (void)M; (void)N;
+    const int64_t KB = (K + 127) / 128;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = rows[p], n = cols[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = oracle_e4m3fn_to_f64(qA[m * K + k]) *
+                       oracle_e8m0_to_f64(sA[m * KB + k / 128]);
+            double b = oracle_e4m3fn_to_f64(qB[n * K + k]) *
+                       oracle_e8m0_to_f64(sB[n * KB + k / 128]);
+            acc += a * b;
+        }
+        if (out64) out64[p] = acc;
+        if (out) out[p] = oracle_f64_to_bf16(acc);
+    }
+}
+
+/* Number of OpenMP threads a parallel region of this library would use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the tiled dense GEMM.
+
+This module only *produces inputs*; it holds none of the GEMM's arithmetic.
+Both the CPU oracle (``oracle/``) and the GPU library receive the arrays made
+here, as raw bit patterns (numpy ``uint16`` for bf16/fp16, ``uint8`` for the
+fp8 elements and e8m0 scales), so the two sides see identical bytes.
+
+Recipe (the pages draw ``torch.randn`` matrices, TileLang SM100 README,
+"Compilation and Usage"):  a CPU ``torch.Generator`` seeded with ``seed``
+draws A and then B as float32 N(0, 1) samples, which are rounded to the
+input type by torch's own round-to-nearest-even cast.  For the block-scaled
+FP8 workload the float32 samples are quantised per row and per 128 K
+elements: the scale is the smallest power of two 2^e with
+``absmax <= 448 * 2^e``, stored as the e8m0 byte ``e + 127``, and the
+elements are ``x * 2^-e`` cast by torch to OCP ``float8_e4m3fn``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+FP8_E4M3_MAX = 448.0
+SCALE_BLOCK_K = 128
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str          # "bf16_nt" | "f16_nn" | "mxfp8_nt"
+    M: int
+    N: int
+    K: int
+    description: str
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The five workloads this library is checked and measured on.
+WORKLOADS = {
+    w.name: w for w in (
+        Workload("bf16_nt_256", "bf16_nt", 256, 256, 256,
+                 "bf16 NT GEMM M=N=K=256"),
+        Workload("f16_nn_1024", "f16_nn", 1024, 1024, 1024,
+                 "fp16 NN GEMM M=N=K=1024"),
+        Workload("bf16_nt_4096x4096x8192", "bf16_nt", 4096, 4096, 8192,
+                 "bf16 NT GEMM M=4096 N=4096 K=8192"),
+        Workload("bf16_nt_4000x3000x5000", "bf16_nt", 4000, 3000, 5000,
+                 "bf16 NT GEMM M=4000 N=3000 K=5000 (ragged tails)"),
+        Workload("mxfp8_nt_4096", "mxfp8_nt", 4096, 4096, 4096,
+                 "block-scaled fp8 (e4m3 + e8m0 per 128 K) NT GEMM M=N=K=4096"),
+    )
+}
+
+
+def generator(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def randn_f32(shape, g: torch.Generator) -> torch.Tensor:
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """Bit patterns of a CPU bf16/fp16 tensor as numpy uint16."""
+    assert t.dtype in (torch.bfloat16, torch.float16)
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def randn_bits(shape, dtype: torch.dtype, g: torch.Generator) -> np.ndarray:
+    return to_bits(randn_f32(shape, g).to(dtype))
+
+
+def quantize_mxfp8(x: torch.Tensor):
+    """Quantise float32 rows to e4m3fn bytes with one e8m0 scale per 128 K.
+
+    Returns (q uint8 (R, K), scales uint8 (R, ceil(K/128))).  The scale of a
+    block is the smallest 2^e with absmax <= 448 * 2^e (found from the exact
+    binary exponent of absmax, no log2), clamped to e in [-127, 127]; an
+    all-zero block gets e = -127 (byte 0).  Elements are x * 2^-e, which is
+    exact, cast once to e4m3fn by torch (round to nearest even).
+    """
+    assert x.dtype == torch.float32 and x.dim() == 2
+    R, K = x.shape
+    KB = (K + SCALE_BLOCK_K - 1) // SCALE_BLOCK_K
+    pad = KB * SCALE_BLOCK_K - K
+    xp = torch.nn.functional.pad(x, (0, pad)) if pad else x
+    absmax = xp.view(R, KB, SCALE_BLOCK_K).abs().amax(dim=2).double().numpy()
+    frac, exp = np.frexp(absmax)                 # absmax = frac * 2^exp, frac in [0.5, 1)
+    # absmax / 2^(exp-9) = frac * 512 in [256, 512): <= 448 iff frac <= 0.875.
+    e = exp.astype(np.int64) - 9 + (frac > FP8_E4M3_MAX / 512.0)
+    e = np.where(absmax == 0.0, -127, e)
+    e = np.clip(e, -127, 127)
+    scales = (e + 127).astype(np.uint8)
+    mult = torch.from_numpy(np.ldexp(1.0, -e)).float()            # 2^-e, exact in fp32
+    y = xp.view(R, KB, SCALE_BLOCK_K) * mult[:, :, None]
+    q = y.reshape(R, KB * SCALE_BLOCK_K)[:, :K].to(torch.float8_e4m3fn)
+    return q.contiguous().view(torch.uint8).numpy().copy(), scales
+
+
+def make_inputs(w: Workload | str, seed: int = 0):
+    """Inputs of a workload as a dict of numpy bit-pattern arrays.
+
+    bf16_nt: A (M,K), B (N,K) uint16.   f16_nn: A (M,K), B (K,N) uint16.
+    mxfp8_nt: qA (M,K), qB (N,K) uint8 and sA (M,KB), sB (N,KB) uint8.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    return make_random(w.kind, w.M, w.N, w.K, seed)
+
+
+def make_random(kind: str, M: int, N: int, K: int, seed: int = 0):
+    g = generator(seed)
+    if kind == "bf16_nt":
+        return {"A": randn_bits((M, K), torch.bfloat16, g),
+                "B": randn_bits((N, K), torch.bfloat16, g)}
+    if kind == "f16_nn":
+        return {"A": randn_bits((M, K), torch.float16, g),
+                "B": randn_bits((K, N), torch.float16, g)}
+    if kind == "mxfp8_nt":
+        a = randn_f32((M, K), g)
+        b = randn_f32((N, K), g)
+        qA, sA = quantize_mxfp8(a)
+        qB, sB = quantize_mxfp8(b)
+        return {"qA": qA, "qB": qB, "sA": sA, "sB": sB}
+    raise ValueError(kind)
+
+
+def make_integer(kind: str, M: int, N: int, K: int, seed: int = 0, lo: int = -2, hi: int = 2):
+    """Integer-valued inputs in [lo, hi] (exact in every input type).
+
+    With |values| <= 2 and K <= 2^21 every partial sum is an integer below
+    2^24, so an fp32 accumulator is exact whatever the summation order.
+    For mxfp8 every scale is 2^0 (byte 127).
+    """
+    g = generator(seed)
+
+    def ints(shape):
+        return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32).float()
+
+    if kind == "bf16_nt":
+        return {"A": to_bits(ints((M, K)).bfloat16()), "B": to_bits(ints((N, K)).bfloat16())}
+    if kind == "f16_nn":
+        return {"A": to_bits(ints((M, K)).half()), "B": to_bits(ints((K, N)).half())}
+    if kind == "mxfp8_nt":
+        KB = (K + SCALE_BLOCK_K - 1) // SCALE_BLOCK_K
+        qA = ints((M, K)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        qB = ints((N, K)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        return {"qA": qA, "qB": qB,
+                "sA": np.full((M, KB), 127, np.uint8), "sB": np.full((N, KB), 127, np.uint8)}
+    raise ValueError(kind)
+
+
+def sample_positions(M: int, N: int, count: int, seed: int = 1):
+    """Output positions for sampled checks: the four corners, the last row and
+    column, and ``count`` seeded uniform positions."""
+    rng = np.random.default_rng(seed)
+    fixed = [(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)]
+    fixed += [(M - 1, int(n)) for n in rng.integers(0, N, 8)]
+    fixed += [(int(m), N - 1) for m in rng.integers(0, M, 8)]
+    rows = np.concatenate([np.array([p[0] for p in fixed]), rng.integers(0, M, count)])
+    cols = np.concatenate([np.array([p[1] for p in fixed]), rng.integers(0, N, count)])
+    return rows.astype(np.int64), cols.astype(np.int64)
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def tflops(M: int, N: int, K: int, seconds: float) -> float:
+    """2*M*N*K / t in TFLOP/s (the pages' throughput formula)."""
+    return 2.0 * M * N * K / seconds / 1e12 if seconds > 0 else math.inf
