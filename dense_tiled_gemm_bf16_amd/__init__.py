@@ -1,0 +1,147 @@
+"""Python binding of libtgemm.so, the tiled dense GEMM library for MI355X.
+
+Argument marshalling only: every step of the GEMM runs in the library's
+gfx950 kernels.  The functions here check tensor dtypes, shapes and
+contiguity, allocate the output when none is given, and call the C entry
+point of the same name on the current HIP stream.  There is no fallback:
+if libtgemm.so is missing the import of the library fails loudly.
+
+The C ABI itself is declared in include/tgemm.h; ``lib()`` returns the
+ctypes handle with those signatures for callers that hold raw pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libtgemm.so")
+
+OK, EINVAL, EALIGN, ETOOBIG, EHIP = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class TgemmError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtgemm.so with argument types set (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m dense_tiled_gemm_bf16_amd.build` "
+            "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    L.gemm_bf16_nt.argtypes = [i64, i64, i64, p, p, p, p]
+    L.gemm_f16_nn.argtypes = [i64, i64, i64, p, p, p, p]
+    L.gemm_mxfp8_nt.argtypes = [i64, i64, i64, p, p, p, p, p, p]
+    for f in (L.gemm_bf16_nt, L.gemm_f16_nn, L.gemm_mxfp8_nt):
+        f.restype = ctypes.c_int
+    L.tgemm_init.argtypes = []
+    L.tgemm_init.restype = ctypes.c_int
+    L.tgemm_last_error.argtypes = []
+    L.tgemm_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().tgemm_last_error().decode()
+
+
+def check(rc: int) -> None:
+    if rc != OK:
+        raise TgemmError(rc, last_error())
+
+
+def init() -> None:
+    check(lib().tgemm_init())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, name, dtype, shape):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major, packed)")
+
+
+def _out(out, shape, dtype, like):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _want(out, "out", dtype, shape)
+    return out
+
+
+def gemm_bf16_nt(a, b, out=None, stream=None):
+    """C = a @ b.T for bf16 a (M,K), b (N,K) -> bf16 (M,N), fp32 accumulation."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    _want(a, "a", torch.bfloat16, (M, K))
+    _want(b, "b", torch.bfloat16, (N, K))
+    c = _out(out, (M, N), torch.bfloat16, a)
+    check(lib().gemm_bf16_nt(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    return c
+
+
+def gemm_f16_nn(a, b, out=None, stream=None):
+    """C = a @ b for fp16 a (M,K), b (K,N) -> fp16 (M,N), fp32 accumulation."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[1]
+    _want(a, "a", torch.float16, (M, K))
+    _want(b, "b", torch.float16, (K, N))
+    c = _out(out, (M, N), torch.float16, a)
+    check(lib().gemm_f16_nn(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    return c
+
+
+def gemm_mxfp8_nt(a, b, scale_a, scale_b, out=None, stream=None):
+    """Block-scaled FP8 NT GEMM -> bf16 (M,N).
+
+    a (M,K), b (N,K): e4m3fn elements (torch.float8_e4m3fn or uint8 bytes);
+    scale_a (M,ceil(K/128)), scale_b (N,ceil(K/128)): e8m0 bytes (uint8).
+    """
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    KB = (K + 127) // 128
+    if a.dtype == torch.float8_e4m3fn:
+        a = a.view(torch.uint8)
+    if b.dtype == torch.float8_e4m3fn:
+        b = b.view(torch.uint8)
+    _want(a, "a", torch.uint8, (M, K))
+    _want(b, "b", torch.uint8, (N, K))
+    _want(scale_a, "scale_a", torch.uint8, (M, KB))
+    _want(scale_b, "scale_b", torch.uint8, (N, KB))
+    c = _out(out, (M, N), torch.bfloat16, a)
+    check(lib().gemm_mxfp8_nt(M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
+                              scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    return c

@@ -1,0 +1,175 @@
+// C-ABI front end of libtgemm.so: argument validation, per-device set-up,
+// error reporting and dispatch to the gfx950 kernels.
+//
+// The convention follows the host wrapper printed on the velog "tilelang"
+// page (1.3 Code Generation & Runtime): an init step, a call that takes raw
+// device pointers and a stream and returns 0 or a negative status, and a
+// get-last-error string.  The argument checks mirror that page's Host
+// IRModule (non-NULL data pointers, packed row-major strides, vectorised
+// dimensions divisible by 8), but the sizes are runtime arguments here.
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/tgemm.h"
+#include "tgemm_internal.hpp"
+
+namespace {
+
+thread_local char g_err[1024];
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+int g_dev_status[kMaxDevices];  // 0 ok, else TGEMM_EHIP
+char g_dev_msg[kMaxDevices][256];
+
+void init_device(int dev) {
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    g_dev_status[dev] = TGEMM_EHIP;
+    snprintf(g_dev_msg[dev], sizeof g_dev_msg[dev], "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
+    return;
+  }
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    g_dev_status[dev] = TGEMM_EHIP;
+    snprintf(g_dev_msg[dev], sizeof g_dev_msg[dev], "device %d is %s; this library runs on gfx950 (MI355X) only",
+             dev, prop.gcnArchName);
+    return;
+  }
+  g_dev_status[dev] = TGEMM_OK;
+}
+
+// Current device, set up once.  Returns TGEMM_OK or TGEMM_EHIP (message set).
+int ensure_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TGEMM_EHIP, "no usable HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TGEMM_EHIP, "device index %d out of range", dev);
+  std::call_once(g_once[dev], init_device, dev);
+  if (g_dev_status[dev] != TGEMM_OK) return fail(g_dev_status[dev], "%s", g_dev_msg[dev]);
+  return TGEMM_OK;
+}
+
+bool overlaps(const void *p, uint64_t pn, const void *q, uint64_t qn) {
+  if (!p || !q || pn == 0 || qn == 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + qn && b < a + pn;
+}
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+constexpr uint64_t kOffsetLimit = 0x7fffffffull;  // the kernels use 31-bit buffer offsets
+
+struct Operand {
+  const char *name;
+  const void *ptr;
+  uint64_t bytes;
+  bool aligned16;  // must be 16-byte aligned
+};
+
+int check_common(const char *fn, int64_t M, int64_t N, int64_t K, int k_multiple, const Operand *ops, int nops,
+                 const void *C, uint64_t c_bytes) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(TGEMM_EINVAL, "%s: negative size (M=%lld, N=%lld, K=%lld)", fn, (long long)M, (long long)N,
+                (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(TGEMM_ETOOBIG, "%s: sizes must be below 2^31 (M=%lld, N=%lld, K=%lld)", fn, (long long)M,
+                (long long)N, (long long)K);
+  if (M == 0 || N == 0) return TGEMM_OK;
+  if (K % k_multiple != 0)
+    return fail(TGEMM_EALIGN, "%s: K=%lld must be a multiple of %d", fn, (long long)K, k_multiple);
+  if (N % 8 != 0) return fail(TGEMM_EALIGN, "%s: N=%lld must be a multiple of 8", fn, (long long)N);
+  if (!C) return fail(TGEMM_EINVAL, "%s: C is NULL", fn);
+  if (misaligned(C)) return fail(TGEMM_EALIGN, "%s: C is not 16-byte aligned", fn);
+  for (int i = 0; i < nops; ++i) {
+    if (ops[i].bytes == 0) continue;  // an empty operand (K == 0) is never read
+    if (!ops[i].ptr) return fail(TGEMM_EINVAL, "%s: %s is NULL", fn, ops[i].name);
+    if (ops[i].aligned16 && misaligned(ops[i].ptr))
+      return fail(TGEMM_EALIGN, "%s: %s is not 16-byte aligned", fn, ops[i].name);
+    if (overlaps(C, c_bytes, ops[i].ptr, ops[i].bytes))
+      return fail(TGEMM_EINVAL, "%s: C overlaps %s", fn, ops[i].name);
+  }
+  return TGEMM_OK;
+}
+
+int dispatch(const char *fn, const tgemm::Problem &p) {
+  int rc = ensure_device();
+  if (rc != TGEMM_OK) return rc;
+  hipError_t e = tgemm::launch(p);
+  if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return TGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tgemm_init(void) {
+  g_err[0] = '\0';
+  return ensure_device();
+}
+
+const char *tgemm_last_error(void) { return g_err; }
+
+int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C, hipStream_t stream) {
+  static const char fn[] = "gemm_bf16_nt";
+  g_err[0] = '\0';
+  const uint64_t m = M > 0 ? (uint64_t)M : 0, n = N > 0 ? (uint64_t)N : 0, k = K > 0 ? (uint64_t)K : 0;
+  const Operand ops[] = {{"A", A, m * k * 2, true}, {"B", B, n * k * 2, true}};
+  int rc = check_common(fn, M, N, K, 8, ops, 2, C, m * n * 2);
+  if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
+  if ((uint64_t)tgemm::kTileM * k * 2 > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
+  tgemm::Problem p{tgemm::Kind::kBf16NT, M, N, K, A, B, nullptr, nullptr, C, stream};
+  return dispatch(fn, p);
+}
+
+int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C, hipStream_t stream) {
+  static const char fn[] = "gemm_f16_nn";
+  g_err[0] = '\0';
+  const uint64_t m = M > 0 ? (uint64_t)M : 0, n = N > 0 ? (uint64_t)N : 0, k = K > 0 ? (uint64_t)K : 0;
+  const Operand ops[] = {{"A", A, m * k * 2, true}, {"B", B, k * n * 2, true}};
+  int rc = check_common(fn, M, N, K, 8, ops, 2, C, m * n * 2);
+  if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
+  if ((uint64_t)tgemm::kTileM * k * 2 > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
+  if (k * n * 2 > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: B too large (K * N * 2 bytes must stay below 2^31)", fn);
+  tgemm::Problem p{tgemm::Kind::kF16NN, M, N, K, A, B, nullptr, nullptr, C, stream};
+  return dispatch(fn, p);
+}
+
+int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *scale_A,
+                  const void *scale_B, void *C, hipStream_t stream) {
+  static const char fn[] = "gemm_mxfp8_nt";
+  g_err[0] = '\0';
+  const uint64_t m = M > 0 ? (uint64_t)M : 0, n = N > 0 ? (uint64_t)N : 0, k = K > 0 ? (uint64_t)K : 0;
+  const uint64_t kb = (k + 127) / 128;
+  const Operand ops[] = {{"A", A, m * k, true},
+                         {"B", B, n * k, true},
+                         {"scale_A", scale_A, m * kb, false},
+                         {"scale_B", scale_B, n * kb, false}};
+  int rc = check_common(fn, M, N, K, 16, ops, 4, C, m * n * 2);
+  if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
+  if ((uint64_t)tgemm::kTileM * k > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K bytes must stay below 2^31)", fn, (long long)K);
+  if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
+  tgemm::Problem p{tgemm::Kind::kMxfp8NT, M, N, K, A, B, scale_A, scale_B, C, stream};
+  return dispatch(fn, p);
+}
+
+}  // extern "C"

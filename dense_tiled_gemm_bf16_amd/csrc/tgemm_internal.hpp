@@ -1,0 +1,30 @@
+// Internal interface between the C-ABI front end (tgemm_abi.cpp) and the
+// gfx950 kernels (tgemm_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace tgemm {
+
+enum class Kind : int { kBf16NT = 0, kF16NN = 1, kMxfp8NT = 2 };
+
+// A validated problem: sizes are non-negative and fit the kernels' limits,
+// pointers are aligned, M > 0 and N > 0.
+struct Problem {
+  Kind kind;
+  int64_t M, N, K;
+  const void *A, *B;
+  const void *scale_A, *scale_B;  // mxfp8 only
+  void *C;
+  hipStream_t stream;
+};
+
+// Output tile of one workgroup (rows of C x columns of C).
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+
+// Enqueues the kernel for `p` on p.stream.  Returns the launch status.
+hipError_t launch(const Problem &p);
+
+}  // namespace tgemm

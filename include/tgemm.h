@@ -1,0 +1,136 @@
+/*
+ * tgemm -- tiled dense GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library libtgemm.so.  Every entry point takes the problem
+ * sizes, plain device pointers and a HIP stream; none takes a framework
+ * type.  All matrices are row-major and packed (leading dimension = number
+ * of columns), as in the lowered kernel of the velog "tilelang" page
+ * (1.2 Pass Pipeline, Host IRModule: strides (K, 1) with byte offset 0).
+ *
+ * Ownership: the caller owns and allocates every buffer.  The library keeps
+ * no per-call state, allocates no device memory and never synchronises: an
+ * entry point validates its arguments, enqueues one kernel on `stream`
+ * (NULL = the null stream) and returns.  Errors that happen on the device
+ * after the enqueue surface at the caller's next synchronisation.
+ *
+ * Return values (shared by all entry points):
+ *   TGEMM_OK          0   success (or nothing to do: M == 0 or N == 0)
+ *   TGEMM_EINVAL     -1   negative size, NULL pointer for a non-empty
+ *                         operand, or C overlapping an input buffer
+ *   TGEMM_EALIGN     -2   a pointer not 16-byte aligned, or a size that
+ *                         breaks the vector width (see each entry point)
+ *   TGEMM_ETOOBIG    -3   an operand larger than the kernels' 32-bit
+ *                         buffer offsets can address (see each entry point)
+ *   TGEMM_EHIP       -4   no usable gfx950 device, or a HIP error at
+ *                         initialisation or launch
+ * After a non-zero return, tgemm_last_error() describes the failure.
+ *
+ * Thread safety: entry points may be called from several host threads; the
+ * error message is kept per thread.  Calls on one stream run in order.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TGEMM_API __attribute__((visibility("default")))
+#else
+#define TGEMM_API
+#endif
+
+#define TGEMM_OK 0
+#define TGEMM_EINVAL (-1)
+#define TGEMM_EALIGN (-2)
+#define TGEMM_ETOOBIG (-3)
+#define TGEMM_EHIP (-4)
+
+/*
+ * C = A . B^T  ("NT"), bfloat16 in, fp32 accumulation, bfloat16 out.
+ *
+ * Defined by the TileLang SM100 README, "Code Example": A is (M, K), B is
+ * (N, K), the product uses trans_B = True, the accumulator is "float" and C
+ * is (M, N) bfloat16.
+ *
+ *   A  device pointer, M x K bf16, row-major (row stride K elements)
+ *   B  device pointer, N x K bf16, row-major
+ *   C  device pointer, M x N bf16, row-major; written, never read
+ *
+ * Each output is the fp32 sum over k of A[m][k] * B[n][k] (summation order
+ * unspecified), rounded to nearest-even bf16.  K == 0 writes zeros.
+ * Requirements: K % 8 == 0 and N % 8 == 0 (vector width, as in the lowered
+ * kernel's "divisible by 8" checks on the velog "tilelang" page, Host
+ * IRModule); A, B and C 16-byte aligned; 256 * K * 2 < 2^31.
+ * A and B may be NULL when K == 0.
+ */
+TGEMM_API int gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
+                 const void *A, const void *B, void *C, hipStream_t stream);
+
+/*
+ * C = A . B  ("NN"), fp16 in, fp32 accumulation, fp16 out.
+ *
+ * Defined by the velog "tilelang" page, 1.1 Front-End DSL: A is (M, K),
+ * B is (K, N), the accumulator type is "float" and C is (M, N) float16.
+ *
+ *   A  device pointer, M x K fp16, row-major
+ *   B  device pointer, K x N fp16, row-major (row stride N elements)
+ *   C  device pointer, M x N fp16, row-major; written, never read
+ *
+ * Each output is the fp32 sum over k of A[m][k] * B[k][n], rounded to
+ * nearest-even fp16 (overflow gives +-inf).  K == 0 writes zeros.
+ * Requirements: K % 8 == 0, N % 8 == 0, 16-byte aligned pointers,
+ * 256 * K * 2 < 2^31 and K * N * 2 < 2^31.
+ */
+TGEMM_API int gemm_f16_nn(int64_t M, int64_t N, int64_t K,
+                const void *A, const void *B, void *C, hipStream_t stream);
+
+/*
+ * Block-scaled FP8 ("MXFP8") C = (sA * A) . (sB * B)^T, bf16 out.
+ *
+ * The Blackwell TCGEN05 GEMM tutorial, section "进阶" (Advanced), names a
+ * block-scaled GEMM with one scale factor per 128 K elements for A and for
+ * B.  Elements are OCP FP8 E4M3 ("e4m3fn", bias 7, max 448, no infinities);
+ * scales are OCP E8M0 bytes E meaning 2^(E - 127).
+ *
+ *   A        device pointer, M x K e4m3fn bytes, row-major
+ *   B        device pointer, N x K e4m3fn bytes, row-major
+ *   scale_A  device pointer, M x ceil(K/128) e8m0 bytes, row-major:
+ *            scale_A[m][j] scales A[m][128 j .. 128 j + 127]
+ *   scale_B  device pointer, N x ceil(K/128) e8m0 bytes, row-major
+ *   C        device pointer, M x N bf16, row-major; written, never read
+ *
+ * C[m][n] is the fp32 sum over k of
+ *   A[m][k] * 2^(scale_A[m][k/128] - 127) * B[n][k] * 2^(scale_B[n][k/128] - 127),
+ * rounded to nearest-even bf16.  K == 0 writes zeros.
+ * Requirements: K % 16 == 0, N % 8 == 0, A, B and C 16-byte aligned (the
+ * scale arrays need no alignment), 256 * K < 2^31.
+ */
+TGEMM_API int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K,
+                  const void *A, const void *B,
+                  const void *scale_A, const void *scale_B,
+                  void *C, hipStream_t stream);
+
+/*
+ * Optional, idempotent set-up for the current device: checks that it is a
+ * gfx950 GPU.  Returns TGEMM_OK or TGEMM_EHIP.  Entry points call it
+ * themselves on first use of a device (the host wrapper's init() on the
+ * velog "tilelang" page, 1.3 Code Generation & Runtime, plays this role).
+ */
+TGEMM_API int tgemm_init(void);
+
+/*
+ * Message for the last failing call on this host thread; "" after a
+ * successful call.  The pointer stays valid until the thread's next call.
+ */
+TGEMM_API const char *tgemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

@@ -11,3 +11,15 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; parity tests of the HIP path")
+
+
+@pytest.hookimpl(hookwrapper=True)
+def pytest_runtest_makereport(item, call):
+    """A GPU test that fails with anything but an assertion (a HIP error, a
+    crash surfacing as an exception) stops the session: no further GPU work
+    runs after a device-side failure."""
+    outcome = yield
+    rep = outcome.get_result()
+    if rep.when == "call" and rep.failed and "gpu" in item.keywords:
+        if call.excinfo is not None and not call.excinfo.errisinstance(AssertionError):
+            item.session.shouldstop = "non-assertion failure in a GPU test"

@@ -1,0 +1,140 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/tgemm.h declares, and rejects bad arguments with the documented
+status codes and messages before touching any device.
+
+No test here launches a kernel: every call either fails validation or has
+nothing to do (M == 0 or N == 0).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_tiled_gemm_bf16_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgemm.h")
+
+A16 = 0x10000          # plausible, 16-byte aligned fake device addresses;
+B16 = 0x20000000       # validation rejects the call before any use
+C16 = 0x40000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^TGEMM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_five_entry_points():
+    assert sorted(declared_functions()) == sorted(
+        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "tgemm_init", "tgemm_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = tg.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", tg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
+def test_header_compiles_as_c():
+    src = '#include "tgemm.h"\nint main(void){ return TGEMM_OK; }\n'
+    res = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only",
+                          "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                          "-D__HIP_PLATFORM_AMD__", "-"], input=src, text=True,
+                         capture_output=True)
+    assert res.returncode == 0, res.stderr
+
+
+def _bf16(M, N, K, A=A16, B=B16, C=C16):
+    return tg.lib().gemm_bf16_nt(M, N, K, A, B, C, None)
+
+
+def _f16(M, N, K, A=A16, B=B16, C=C16):
+    return tg.lib().gemm_f16_nn(M, N, K, A, B, C, None)
+
+
+def _mx(M, N, K, A=A16, B=B16, SA=0x30000001, SB=0x30800003, C=C16):
+    return tg.lib().gemm_mxfp8_nt(M, N, K, A, B, SA, SB, C, None)
+
+
+@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+def test_empty_outputs_are_a_no_op(call):
+    # M == 0 or N == 0: nothing to compute, success without any device work,
+    # even with NULL pointers.
+    assert call(0, 16, 16, A=None, B=None, C=None) == tg.OK
+    assert call(16, 0, 16, A=None, B=None, C=None) == tg.OK
+    assert tg.last_error() == ""
+
+
+@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+def test_negative_sizes(call):
+    for dims in [(-1, 16, 16), (16, -8, 16), (16, 16, -16)]:
+        assert call(*dims) == tg.EINVAL
+        assert "negative size" in tg.last_error()
+
+
+@pytest.mark.parametrize("call,kmul", [(_bf16, 8), (_f16, 8), (_mx, 16)])
+def test_vector_width_rules(call, kmul):
+    assert call(16, 16, kmul + kmul // 2) == tg.EALIGN
+    assert f"multiple of {kmul}" in tg.last_error()
+    assert call(16, 12, 64) == tg.EALIGN
+    assert "N=12 must be a multiple of 8" in tg.last_error()
+
+
+@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+def test_null_and_misaligned_pointers(call):
+    assert call(16, 16, 64, A=None) == tg.EINVAL and "A is NULL" in tg.last_error()
+    assert call(16, 16, 64, B=None) == tg.EINVAL and "B is NULL" in tg.last_error()
+    assert call(16, 16, 64, C=None) == tg.EINVAL and "C is NULL" in tg.last_error()
+    assert call(16, 16, 64, A=A16 + 8) == tg.EALIGN and "A is not 16-byte aligned" in tg.last_error()
+    assert call(16, 16, 64, B=B16 + 2) == tg.EALIGN and "B is not 16-byte aligned" in tg.last_error()
+    assert call(16, 16, 64, C=C16 + 4) == tg.EALIGN and "C is not 16-byte aligned" in tg.last_error()
+
+
+def test_mxfp8_scale_pointers():
+    assert _mx(16, 16, 256, SA=None) == tg.EINVAL and "scale_A is NULL" in tg.last_error()
+    assert _mx(16, 16, 256, SB=None) == tg.EINVAL and "scale_B is NULL" in tg.last_error()
+    # Scale arrays need no alignment: odd addresses pass validation up to the
+    # device step, so only a C overlapping them is checked here.
+    assert _mx(16, 16, 256, SA=C16 + 100) == tg.EINVAL and "C overlaps scale_A" in tg.last_error()
+
+
+@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+def test_output_may_not_overlap_inputs(call):
+    M, N, K = 64, 64, 64
+    assert call(M, N, K, C=A16 + 16) == tg.EINVAL and "C overlaps A" in tg.last_error()
+    assert call(M, N, K, C=B16 - 1024 + 16 * 4) == tg.EINVAL and "C overlaps B" in tg.last_error()
+
+
+def test_too_big():
+    # 256 rows of a K-slice panel must fit 31-bit buffer offsets.
+    assert _bf16(16, 16, 1 << 22) == tg.ETOOBIG and "too large" in tg.last_error()
+    assert _mx(16, 16, 1 << 23) == tg.ETOOBIG and "too large" in tg.last_error()
+    far = 0x7F0000000000     # C far from the (fake, 4 GiB) B
+    assert _f16(16, 1 << 16, 1 << 15, C=far) == tg.ETOOBIG and "B too large" in tg.last_error()
+    assert _bf16(1 << 31, 16, 16) == tg.ETOOBIG and "below 2^31" in tg.last_error()
+
+
+def test_error_message_resets_after_success():
+    assert _bf16(-1, 1, 1) == tg.EINVAL and tg.last_error() != ""
+    assert _bf16(0, 8, 8) == tg.OK and tg.last_error() == ""
+
+
+def test_python_wrapper_raises_with_code():
+    with pytest.raises(tg.TgemmError) as e:
+        tg.check(_bf16(-1, 1, 1))
+    assert e.value.code == tg.EINVAL
+
+
+def test_no_device_is_an_error_not_a_crash():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the no-device path cannot be exercised")
+    assert tg.lib().tgemm_init() == tg.EHIP
+    assert "HIP device" in tg.last_error() or "hip" in tg.last_error().lower()

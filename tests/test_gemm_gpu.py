@@ -1,0 +1,260 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerance: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| elementwise on the output
+values, NaN failing -- the check the pages themselves apply (TileLang SM100
+README, "Compilation and Usage"), here against the binary64 oracle rounded
+once to the output type.  On integer-valued inputs every fp32 partial sum
+is exact, so there the GPU and the oracle must agree bit for bit.
+
+Small shapes are compared in full; the large workloads are compared on
+sampled outputs plus whole rows and columns computed one output at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_gemm_bf16_amd as tg
+import oracle
+import workloads
+from _exact import bf16_values, f16_values
+
+pytestmark = pytest.mark.gpu
+
+RTOL = ATOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    tg.init()
+
+
+# --- helpers ---------------------------------------------------------------------
+
+def to_dev(bits: np.ndarray, kind: str) -> torch.Tensor:
+    if bits.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        t = t.view(torch.bfloat16 if kind == "bf16" else torch.float16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(bits))
+    return t.cuda()
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run(kind: str, x: dict, M: int, N: int, K: int, out=None, stream=None) -> torch.Tensor:
+    print(f"[gpu] {kind} M={M} N={N} K={K}", flush=True)
+    if kind == "bf16_nt":
+        c = tg.gemm_bf16_nt(to_dev(x["A"], "bf16"), to_dev(x["B"], "bf16"), out=out, stream=stream)
+    elif kind == "f16_nn":
+        c = tg.gemm_f16_nn(to_dev(x["A"], "f16"), to_dev(x["B"], "f16"), out=out, stream=stream)
+    else:
+        c = tg.gemm_mxfp8_nt(to_dev(x["qA"], ""), to_dev(x["qB"], ""), to_dev(x["sA"], ""),
+                             to_dev(x["sB"], ""), out=out, stream=stream)
+    torch.cuda.synchronize()
+    return c
+
+
+def oracle_full(kind, x):
+    if kind == "bf16_nt":
+        return oracle.gemm_bf16_nt(x["A"], x["B"])
+    if kind == "f16_nn":
+        return oracle.gemm_f16_nn(x["A"], x["B"])
+    return oracle.gemm_mxfp8_nt(x["qA"], x["qB"], x["sA"], x["sB"])
+
+
+def oracle_at(kind, x, rows, cols):
+    if kind == "bf16_nt":
+        return oracle.gemm_bf16_nt_at(x["A"], x["B"], rows, cols)
+    if kind == "f16_nn":
+        return oracle.gemm_f16_nn_at(x["A"], x["B"], rows, cols)
+    return oracle.gemm_mxfp8_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols)
+
+
+def values(kind, bits):
+    return f16_values(bits) if kind == "f16_nn" else bf16_values(bits)
+
+
+def assert_close(kind, got_bits, ref_bits, what=""):
+    g, r = values(kind, got_bits), values(kind, ref_bits)
+    bad = ~(np.abs(g - r) <= ATOL + RTOL * np.abs(r))
+    if bad.any():
+        idx = np.argwhere(bad)[:8]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside rtol=atol=1e-2; first at "
+            f"{[tuple(int(v) for v in i) for i in idx]}: got {g[bad][:8]} want {r[bad][:8]}")
+
+
+def assert_bitwise(got_bits, ref_bits, what=""):
+    diff = got_bits != ref_bits
+    if diff.any():
+        idx = np.argwhere(diff)[:8]
+        raise AssertionError(f"{what}: {int(diff.sum())} of {diff.size} differ; first at "
+                             f"{[tuple(int(v) for v in i) for i in idx]}: got {got_bits[diff][:8]} "
+                             f"want {ref_bits[diff][:8]}")
+
+
+def full_rows_cols(M, N, count=2000, seed=1):
+    """Sampled positions plus every output of a few whole rows and columns
+    (first, last, and tile edges)."""
+    rows, cols = workloads.sample_positions(M, N, count, seed)
+    r_full = sorted({0, min(255, M - 1), min(256, M - 1), M - 1})
+    c_full = sorted({0, min(255, N - 1), min(256, N - 1), N - 1})
+    rr = [rows] + [np.full(N, r) for r in r_full] + [np.arange(M) for _ in c_full]
+    cc = [cols] + [np.arange(N) for _ in r_full] + [np.full(M, c) for c in c_full]
+    return np.concatenate(rr).astype(np.int64), np.concatenate(cc).astype(np.int64)
+
+
+# --- the five workloads -----------------------------------------------------------
+
+SMALL = ["bf16_nt_256", "f16_nn_1024"]
+LARGE = ["bf16_nt_4096x4096x8192", "bf16_nt_4000x3000x5000", "mxfp8_nt_4096"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workload_full_parity(name):
+    w = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(w)
+    got = to_bits(run(w.kind, x, w.M, w.N, w.K))
+    assert_close(w.kind, got, oracle_full(w.kind, x), name)
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_workload_sampled_parity(name):
+    w = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(w)
+    got = to_bits(run(w.kind, x, w.M, w.N, w.K))
+    rows, cols = full_rows_cols(w.M, w.N)
+    assert_close(w.kind, got[rows, cols], oracle_at(w.kind, x, rows, cols), name)
+    assert np.isfinite(values(w.kind, got)).all()
+
+
+@pytest.mark.parametrize("name", SMALL + LARGE)
+def test_workload_integer_inputs_bitwise(name):
+    w = workloads.WORKLOADS[name]
+    x = workloads.make_integer(w.kind, w.M, w.N, w.K, seed=5)
+    got = to_bits(run(w.kind, x, w.M, w.N, w.K))
+    if name in SMALL:
+        assert_bitwise(got, oracle_full(w.kind, x), name)
+    else:
+        rows, cols = full_rows_cols(w.M, w.N)
+        assert_bitwise(got[rows, cols], oracle_at(w.kind, x, rows, cols), name)
+
+
+# --- tails, several tiles, degenerate shapes ------------------------------------------
+
+TAIL_M = [1, 31, 255, 257, 300]
+TAIL_N = [8, 56, 264]
+
+
+@pytest.mark.parametrize("K", [8, 64, 72, 136, 520])
+def test_bf16_nt_tails(K):
+    for M in TAIL_M:
+        for N in TAIL_N:
+            x = workloads.make_random("bf16_nt", M, N, K, seed=M * 7 + N * 3 + K)
+            assert_close("bf16_nt", to_bits(run("bf16_nt", x, M, N, K)), oracle_full("bf16_nt", x),
+                         f"bf16_nt {M}x{N}x{K}")
+            xi = workloads.make_integer("bf16_nt", M, N, K, seed=M + N + K)
+            assert_bitwise(to_bits(run("bf16_nt", xi, M, N, K)), oracle_full("bf16_nt", xi),
+                           f"bf16_nt int {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("K", [8, 64, 72, 200])
+def test_f16_nn_tails(K):
+    for M in TAIL_M:
+        for N in TAIL_N:
+            x = workloads.make_random("f16_nn", M, N, K, seed=M * 7 + N * 3 + K)
+            assert_close("f16_nn", to_bits(run("f16_nn", x, M, N, K)), oracle_full("f16_nn", x),
+                         f"f16_nn {M}x{N}x{K}")
+            xi = workloads.make_integer("f16_nn", M, N, K, seed=M + N + K)
+            assert_bitwise(to_bits(run("f16_nn", xi, M, N, K)), oracle_full("f16_nn", xi),
+                           f"f16_nn int {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("K", [16, 112, 128, 144, 400])
+def test_mxfp8_tails(K):
+    for M in TAIL_M:
+        for N in TAIL_N:
+            x = workloads.make_random("mxfp8_nt", M, N, K, seed=M * 7 + N * 3 + K)
+            assert_close("mxfp8_nt", to_bits(run("mxfp8_nt", x, M, N, K)), oracle_full("mxfp8_nt", x),
+                         f"mxfp8 {M}x{N}x{K}")
+            xi = workloads.make_integer("mxfp8_nt", M, N, K, seed=M + N + K)
+            assert_bitwise(to_bits(run("mxfp8_nt", xi, M, N, K)), oracle_full("mxfp8_nt", xi),
+                           f"mxfp8 int {M}x{N}x{K}")
+
+
+def test_mxfp8_per_row_and_per_block_scales_bitwise():
+    """Integer elements with a different power-of-two scale per row and per
+    128-K block: exact in fp32, so bitwise; a wrong scale lane, row or block
+    mapping shows up here."""
+    M, N, K = 300, 264, 512
+    x = workloads.make_integer("mxfp8_nt", M, N, K, seed=9)
+    rng = np.random.default_rng(3)
+    x["sA"] = rng.integers(124, 131, x["sA"].shape).astype(np.uint8)
+    x["sB"] = rng.integers(124, 131, x["sB"].shape).astype(np.uint8)
+    assert_bitwise(to_bits(run("mxfp8_nt", x, M, N, K)), oracle_full("mxfp8_nt", x), "mxfp8 scales")
+
+
+@pytest.mark.parametrize("kind", ["bf16_nt", "f16_nn", "mxfp8_nt"])
+def test_mid_size_full_parity_several_tiles(kind):
+    M, N, K = 776, 520, 1040 if kind != "mxfp8_nt" else 1024
+    x = workloads.make_random(kind, M, N, K, seed=11)
+    assert_close(kind, to_bits(run(kind, x, M, N, K)), oracle_full(kind, x), f"{kind} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kind", ["bf16_nt", "f16_nn", "mxfp8_nt"])
+def test_K_zero_writes_zeros(kind):
+    M, N = 70, 40
+    x = {"A": np.zeros((M, 0), np.uint16), "B": np.zeros((N, 0) if kind == "bf16_nt" else (0, N), np.uint16),
+         "qA": np.zeros((M, 0), np.uint8), "qB": np.zeros((N, 0), np.uint8),
+         "sA": np.zeros((M, 0), np.uint8), "sB": np.zeros((N, 0), np.uint8)}
+    dt = torch.float16 if kind == "f16_nn" else torch.bfloat16
+    out = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    got = to_bits(run(kind, x, M, N, 0, out=out))
+    assert np.all(got == 0)
+
+
+def test_output_guard_band_untouched():
+    """C inside a larger buffer: nothing outside C's M x N elements changes."""
+    M, N, K = 300, 264, 136
+    x = workloads.make_random("bf16_nt", M, N, K, seed=2)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), 1.5, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + M * N].view(M, N)
+    run("bf16_nt", x, M, N, K, out=out)
+    b = buf.cpu()
+    assert torch.all(b[:pad] == 1.5) and torch.all(b[pad + M * N:] == 1.5)
+    assert_close("bf16_nt", to_bits(out), oracle_full("bf16_nt", x), "guard band")
+
+
+def test_deterministic_bitwise():
+    w = workloads.WORKLOADS["bf16_nt_4000x3000x5000"]
+    x = workloads.make_inputs(w)
+    a, b = to_dev(x["A"], "bf16"), to_dev(x["B"], "bf16")
+    c1 = tg.gemm_bf16_nt(a, b)
+    c2 = tg.gemm_bf16_nt(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+def test_non_default_stream():
+    M, N, K = 512, 512, 512
+    x = workloads.make_random("bf16_nt", M, N, K, seed=4)
+    s = torch.cuda.Stream()
+    a, b = to_dev(x["A"], "bf16"), to_dev(x["B"], "bf16")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = tg.gemm_bf16_nt(a, b, stream=s)
+    s.synchronize()
+    assert_close("bf16_nt", to_bits(c), oracle_full("bf16_nt", x), "stream")
+
+
+def test_misaligned_device_pointer_is_rejected():
+    a = torch.zeros(64 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    rc = tg.lib().gemm_bf16_nt(64, 64, 64, a.data_ptr() + 2, b.data_ptr(), c.data_ptr(), None)
+    assert rc == tg.EALIGN and "A is not 16-byte aligned" in tg.last_error()
