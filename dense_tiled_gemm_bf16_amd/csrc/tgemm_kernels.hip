@@ -2,9 +2,10 @@
 //
 // One workgroup of 256 threads (4 wave64s in a 2 x 2 grid) computes a
 // 256 x 256 tile of C; each wave owns a 128 x 128 sub-tile held as 4 x 4
-// blocks of 32 x 32 fp32 accumulators (256 per lane).  The K loop walks
-// 128-byte slices of the A and B row panels (64 bf16/fp16 or 128 fp8
-// elements per row), double-buffered in LDS.
+// blocks of 32 x 32 fp32 accumulators (256 per lane, in AGPRs).  The K loop
+// walks 64-byte slices of the A and B panels (32 bf16/fp16 or 64 fp8
+// elements per row) through a ring of four LDS slots, loading three slices
+// ahead of the one being multiplied.
 //
 // Where this follows the pages and where it departs:
 //  * tile grid: ceil-div over N and M as in the TileLang SM100 README
@@ -16,18 +17,21 @@
 //  * global -> LDS staging: the pages use TMA boxes with a hardware
 //    swizzle (velog "tilelang", 1.2 Host IRModule).  Here every lane moves
 //    16 bytes with a buffer load that writes LDS directly; the 16-byte
-//    chunks of each 128-byte row are XOR-permuted so the MFMA operand reads
-//    hit distinct LDS banks.  Out-of-range rows and the ragged K tail read
-//    as zero through the buffer descriptor's range check (the pages' TMA
-//    zero OOB fill).
+//    chunks of each row are XOR-permuted so the MFMA operand reads hit
+//    distinct LDS banks.  Out-of-range rows and the ragged K tail take an
+//    out-of-range buffer offset and arrive as zeros (the pages' TMA zero
+//    OOB fill).
 //  * pipelined K loop: the pages use a 3-slot ring with producer and
 //    consumer warpgroups and mbarrier parity waits (velog "tilelang",
-//    Device IRModule).  Here every wave both loads and computes: while the
-//    MFMAs read slot s, the loads for the next K slice fill slot s^1; one
-//    s_waitcnt + s_barrier per slice closes the step.
+//    Device IRModule).  Here every wave both loads and computes: a 4-slot
+//    ring, loads issued 3 slices ahead and spread evenly between MFMAs, one
+//    s_waitcnt + s_barrier per slice placed so that the first operand reads
+//    of the next slice overlap the last MFMAs of the current one.
 //  * wave-tile MMA: v_mfma_f32_32x32x16_{bf16,f16} and, for the
 //    block-scaled path, v_mfma_scale_f32_32x32x64_f8f6f4 with the e8m0
 //    block scales as operands (TCGEN05 tutorial, "进阶" (Advanced)).
+//  * NN: B stays K x N in LDS and is read with the LDS transpose read
+//    (ds_read_b64_tr_b16), which hands each lane four K values of one column.
 //  * epilogue: fp32 -> bf16/fp16 with round-to-nearest-even, masked stores.
 //    The MFMA is fed B rows as its first operand and A rows as its second,
 //    so each lane's accumulators hold 4 consecutive columns of one row of C
@@ -36,6 +40,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "tgemm_internal.hpp"
 
@@ -48,6 +53,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
@@ -55,8 +61,9 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;                  // bytes of one tile row per K slice
-constexpr int kSlotBytes = kTileM * kRowBytes;  // one operand, one slot: 32 KiB
+constexpr int kRowBytes = 64;                   // bytes of one tile row per K slice
+constexpr int kSlotBytes = kTileM * kRowBytes;  // one operand, one slot: 16 KiB
+constexpr int kAhead = 3;                       // slices loaded ahead of the one multiplied
 constexpr uint32_t kOOB = 0x80000000u;          // voffset that is always out of range
 
 static_assert(kTileM == 256 && kTileN == 256, "kernel assumes 256 x 256 tiles");
@@ -96,8 +103,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
-__device__ __forceinline__ void wait_vm0_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// s_waitcnt immediate for vmcnt(vm) expcnt(7) lgkmcnt(0) (gfx9 encoding:
+// vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+}
+
+// Wait states between VALU accesses of accumulators and inline-asm MFMAs,
+// which the compiler's hazard tracking does not see: 24 idle cycles cover
+// the longest MFMA result latency of the forms used here.
+__device__ __forceinline__ void mfma_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Workgroup barrier that orders LDS traffic for the compiler but leaves the
 // hardware waits to the caller (no fence, so no implicit vmcnt(0)).
@@ -107,11 +128,16 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Chunk permutation inside a 128-byte tile row: row r keeps its logical
-// 16-byte chunk c at physical chunk c ^ swz(r).  Any 16 consecutive rows
-// read at one logical chunk land on 16 distinct (chunk, row parity) pairs,
-// i.e. on distinct banks for both 128-byte and 256-byte bank periods.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk permutation inside a 64-byte tile row: row r keeps logical 16-byte
+// chunk c at physical chunk c ^ swz(r).  Eight consecutive rows read at one
+// logical chunk land on 8 distinct 16-byte bank groups of a 128-byte bank
+// period, and sixteen on 16 distinct groups of a 256-byte period.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// NN B slot: 32 K rows of 512 bytes (256 columns).  Row k keeps logical
+// chunk c at physical chunk c ^ swz_nn(k), which spreads the four rows read
+// together by a transpose read over distinct bank groups.
+__device__ __forceinline__ int swz_nn(int k) { return (k & 3) << 1; }
 
 // Workgroup id -> output tile.  Consecutive workgroup ids are placed on the
 // 8 XCDs in turn; renumber so that the ids sharing an XCD are consecutive,
@@ -131,243 +157,299 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
 }
 
 // ---------------------------------------------------------------------------
-// Global -> LDS staging of one K slice of a K-contiguous panel (A of every
-// kind, B of the NT kinds).  The slot is 256 rows x 128 bytes.  Wave w moves
-// rows [64 w, 64 w + 64) with 8 instructions of 8 rows each; lane l of
-// instruction i writes LDS bytes [16 l, 16 l + 16) of its 1 KiB row group,
-// i.e. row 64 w + 8 i + l / 8, physical chunk l % 8, and therefore fetches
-// logical chunk (l % 8) ^ swz(row) of that row from global memory.
+// Staging of one K slice of a K-contiguous panel (A of every kind, B of the
+// NT kinds) into a slot of 256 rows x 64 bytes.  Wave w moves rows
+// [64 w, 64 w + 64) with 4 direct-to-LDS instructions of 16 rows each; lane
+// l of instruction i writes LDS bytes [16 l, 16 l + 16) of its 1 KiB row
+// group, i.e. row 64 w + 16 i + l / 4, physical chunk l % 4, and therefore
+// fetches logical chunk (l % 4) ^ swz(row) of that row.  swz depends on the
+// row only through row % 16 = l / 4, so the chunk is the same for all i.
 // ---------------------------------------------------------------------------
 struct PanelLoader {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[8];   // per instruction: byte offset of this lane's chunk at K slice 0
-  int kcol[2];       // element column of this lane's chunk at slice 0 (even / odd i)
+  uint32_t off[4];  // per instruction: byte offset of this lane's chunk at slice 0
+  int kcol;         // element column of this lane's chunk inside a slice
 
-  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int elem,
-                                       int wave, int lane) {
+  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int elem, int wave,
+                                       int lane) {
     rsrc = make_rsrc(panel, (uint32_t)rows_valid * (uint32_t)K * (uint32_t)elem);
-    const int chunk_elems = 16 / elem;
-    for (int p = 0; p < 2; ++p) kcol[p] = (((lane & 7) ^ (lane >> 3) ^ p)) * chunk_elems;
+    const int c = (lane & 3) ^ swz(lane >> 2);
+    kcol = c * (16 / elem);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave * 64 + i * 8 + (lane >> 3);
-      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem
-                              : kOOB;
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 64 + i * 16 + (lane >> 2);
+      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)elem + (uint32_t)c * 16u : kOOB;
     }
   }
 
-  // Per-slice lane predicate: chunks at or past column K (the ragged last
-  // slice, or a slice past the end) take an out-of-range offset, so the
-  // buffer range check delivers zeros.
-  struct Slice {
-    uint32_t soff;
-    bool ok0, ok1;
-  };
-  __device__ __forceinline__ Slice slice(int kt, int K, int slice_k) const {
-    const int k0 = kt * slice_k;
-    return Slice{(uint32_t)kt * kRowBytes, k0 + kcol[0] < K, k0 + kcol[1] < K};
-  }
-  // Instruction i of slice `sl`: 8 rows x 128 bytes straight into LDS.
-  __device__ __forceinline__ void issue_one(LDS_AS uint8_t *slot, int wave, const Slice &sl, int i) const {
-    const uint32_t o = ((i & 1) ? sl.ok1 : sl.ok0) ? off[i] : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + wave * 8192 + i * 1024), 16, o,
-                                             sl.soff, 0, 0);
+  // Instruction i of slice kt.  A chunk at or past column K (the ragged last
+  // slice, or a slice past the end) takes an out-of-range offset.
+  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k, int i) const {
+    const bool ok = kt * slice_k + kcol < K;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + wave * 4096 + i * 1024), 16,
+                                             ok ? off[i] : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
   }
 };
 
 // ---------------------------------------------------------------------------
-// NN B operand (K x N, N-contiguous).  Thread t owns an 8 x 8 block: rows
-// k = 8 (t / 32) .. +8 of the slice, columns n = 8 (t % 32) .. +8 of the tile.
-// It loads the 8 row pieces (16 bytes each, coalesced across the wave),
-// transposes the block in registers and writes 8 LDS rows (one per column n)
-// of 8 K values, in the same swizzled [n][k] layout as an NT B slot.
+// Staging of one K slice of the NN B operand (K x N, N-contiguous) into a
+// slot of 32 K rows x 512 bytes.  Wave w moves K rows [8 w, 8 w + 8) with 4
+// instructions of 2 rows each; lane l of instruction i writes row
+// 8 w + 2 i + l / 32, physical chunk l % 32, fetching logical chunk
+// (l % 32) ^ swz_nn(row), i.e. columns n0 + 8 chunk .. + 8.
 // ---------------------------------------------------------------------------
 struct NNLoader {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off0;   // byte offset of row k = 8 (t / 32), column n of this thread, at slice 0
-  uint32_t row_stride;
-  int krow0;       // first k of this thread's block inside a slice
-  bool col_ok;
-  u32x4 v[8];
+  uint32_t off[4];  // per instruction: byte offset at slice 0 (kOOB past N)
+  int krow[4];      // K row inside the slice
+  uint32_t slice_bytes;
 
-  __device__ __forceinline__ void init(const uint8_t *B, int K, int N, int n0, int tid) {
+  __device__ __forceinline__ void init(const uint8_t *B, int K, int N, int n0, int wave, int lane) {
     rsrc = make_rsrc(B, (uint32_t)K * (uint32_t)N * 2u);
-    const int nc = tid & 31;
-    krow0 = (tid >> 5) * 8;
-    const int n = n0 + nc * 8;
-    col_ok = n < N;
-    row_stride = (uint32_t)N * 2u;
-    off0 = (uint32_t)krow0 * row_stride + (uint32_t)n * 2u;
-  }
-
-  // Row j of this thread's block of slice kt (zeros past K or past N).
-  __device__ __forceinline__ void load_one(int kt, int K, int j) {
-    const int k = kt * 64 + krow0 + j;
-    const uint32_t o = (col_ok && k < K) ? off0 + (uint32_t)(kt * 64 + j) * row_stride : kOOB;
-    v[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, 0);
-  }
-
-  __device__ __forceinline__ void store(LDS_AS uint8_t *slot, int tid) const {
-    const int nc = tid & 31, kc = tid >> 5;
+    slice_bytes = 32u * (uint32_t)N * 2u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = i >> 1;
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low fp16 halves
-      u32x4 o;
-      o[0] = __builtin_amdgcn_perm(v[1][d], v[0][d], sel);
-      o[1] = __builtin_amdgcn_perm(v[3][d], v[2][d], sel);
-      o[2] = __builtin_amdgcn_perm(v[5][d], v[4][d], sel);
-      o[3] = __builtin_amdgcn_perm(v[7][d], v[6][d], sel);
-      const int n = nc * 8 + i;
-      *(LDS_AS u32x4 *)(slot + n * kRowBytes + ((kc ^ swz(n)) << 4)) = o;
+    for (int i = 0; i < 4; ++i) {
+      const int kr = wave * 8 + i * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swz_nn(kr);
+      const int n = n0 + c * 8;
+      krow[i] = kr;
+      off[i] = n < N ? (uint32_t)kr * (uint32_t)N * 2u + (uint32_t)n * 2u : kOOB;
     }
+  }
+
+  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int i) const {
+    const bool ok = kt * 32 + krow[i] < K;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + wave * 4096 + i * 1024), 16,
+                                             ok ? off[i] : kOOB, (uint32_t)kt * slice_bytes, 0, 0);
   }
 };
 
+// ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
 struct Slots {
-  LDS_AS uint8_t *a[2];
-  LDS_AS uint8_t *b[2];
+  LDS_AS uint8_t *a[4];
+  LDS_AS uint8_t *b[4];
 };
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 template <int KIND>
 struct Kernel {
   using T = Traits<KIND>;
   static constexpr int kElem = T::kElem;
-  static constexpr int kSliceK = kRowBytes / kElem;     // K elements per slice
-  static constexpr int kSubsteps = T::kScaled ? 2 : 4;  // MFMAs along K per slice
+  static constexpr int kSliceK = kRowBytes / kElem;  // K elements per slice
+  // MFMA shape.  16-bit inputs: v_mfma_f32_16x16x32 (one per 16 x 16 block per
+  // slice; it reads and writes 4 accumulators per 16 K flops, half the
+  // accumulator traffic per flop of the 32 x 32 x 16 form, which costs
+  // power).  fp8: v_mfma_scale_f32_32x32x64 (one per 32 x 32 block).
+  static constexpr int kBlk = T::kScaled ? 32 : 16;
+  static constexpr int kNB = 128 / kBlk;       // blocks per wave along M and along N
+  static constexpr int kMfma = kNB * kNB;      // MFMAs per slice
+  static constexpr int kHalf = kMfma / 2;
+  // Load instructions per thread per slice: 4 for the A panel and 4 for B
+  // (issued three slices ahead, one per kMfma / 8 MFMAs), plus, for the
+  // block-scaled kind, 8 scale bytes (issued one slice ahead, at the start of
+  // the slice before).
+  static constexpr int kLoads = 8;
+  static constexpr int kScaleLoads = T::kScaled ? 8 : 0;
+  // The wait in the middle of slice j must cover the panel loads of slice
+  // j + 1 (issued during slice j - 2).  Issued after them: the panel loads of
+  // slice j + 2, the first half of those of slice j + 3, and the scale loads
+  // made at the starts of slices j - 1 and j.
+  static constexpr int kWaitVm = kLoads + kLoads / 2 + 2 * kScaleLoads;
 
-  // Operand fragment of one 32-row block for one K substep.
   using Frag = typename std::conditional<T::kScaled, i32x8, u32x4>::type;
+  using Acc = typename std::conditional<T::kScaled, f32x16, f32x4>::type;
+  struct Frags {
+    Frag x[kNB], y[kNB];
+  };
 
   const Args &a;
   Slots slots;
-  int tid, lane, wave, wave_m, wave_n, hi, lane_sw;
+  int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
   PanelLoader la, lb;
   NNLoader lnn;
   __amdgpu_buffer_rsrc_t rsa, rsb;
   uint32_t soA[4], soB[4];
-  int sc[2][8];  // per slot: B-row scales of the 4 x blocks, then A-row scales of the 4 y blocks
-  f32x16 acc[4][4];
+  // Scale bytes by slice parity: the B-row scales of the 4 x blocks, then the
+  // A-row scales of the 4 y blocks (each in byte 0 of its register).
+  int sc[2][8];
+  Acc acc[kNB][kNB];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
 
-  __device__ __forceinline__ Frag read_frag(const LDS_AS uint8_t *slot, int row, int sub) const {
-    const LDS_AS uint8_t *p = slot + row * kRowBytes;
+  // Fragment of one block of kBlk rows (B rows = C columns for x, A rows for
+  // y) from a K-contiguous slot.
+  __device__ __forceinline__ Frag read_rows(const LDS_AS uint8_t *slot, int row0) const {
     if constexpr (T::kScaled) {
-      // 32 bytes of K per lane: logical chunks 4 sub + 2 hi and 4 sub + 2 hi + 1.
-      const int c0 = 4 * sub + 2 * hi;
-      u32x4 u = *(const LDS_AS u32x4 *)(p + ((c0 ^ lane_sw) << 4));
-      u32x4 v = *(const LDS_AS u32x4 *)(p + (((c0 + 1) ^ lane_sw) << 4));
+      // 32 x 32 x 64: lane l holds row l % 32, 32 bytes of K: logical chunks
+      // 2 (l / 32) and 2 (l / 32) + 1.
+      const int hi = lane >> 5;
+      const LDS_AS uint8_t *p = slot + (row0 + (lane & 31)) * kRowBytes;
+      u32x4 u = *(const LDS_AS u32x4 *)(p + (((2 * hi) ^ lane_sw) << 4));
+      u32x4 v = *(const LDS_AS u32x4 *)(p + (((2 * hi + 1) ^ lane_sw) << 4));
       i32x8 r;
       r[0] = u[0]; r[1] = u[1]; r[2] = u[2]; r[3] = u[3];
       r[4] = v[0]; r[5] = v[1]; r[6] = v[2]; r[7] = v[3];
       return r;
     } else {
-      // 16 bytes (8 elements) of K per lane: logical chunk 2 sub + hi.
-      const int c = 2 * sub + hi;
-      return *(const LDS_AS u32x4 *)(p + ((c ^ lane_sw) << 4));
+      // 16 x 16 x 32: lane l holds row l % 16, 8 elements of K: logical
+      // chunk l / 16.
+      const LDS_AS uint8_t *p = slot + (row0 + (lane & 15)) * kRowBytes;
+      return *(const LDS_AS u32x4 *)(p + (((lane >> 4) ^ lane_sw) << 4));
     }
   }
 
-  __device__ static __forceinline__ f32x16 mma(const Frag &x, const Frag &y, const f32x16 &c, int sx, int sy) {
+  // NN x fragment: columns n = col0 + l % 16 of the [k][n] B slot, K values
+  // 8 (l / 16) + 0..7.  Each transpose read gives a lane 4 K values of one
+  // column: in a 16-lane group, source lane 4 e + q points at K row base + e,
+  // columns col0 + 4 q .. + 3, and lane i receives column col0 + i.
+  __device__ __forceinline__ Frag read_cols(const LDS_AS uint8_t *slot, int col0) const {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const int n = col0 + 4 * q;
+    u32x4 r;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = 8 * g + 4 * t + e;
+      const LDS_AS uint8_t *p = slot + kr * 512 + ((((n >> 3) ^ swz_nn(kr))) << 4) + (n & 7) * 2;
+      s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)p);
+      u32x2 w = __builtin_bit_cast(u32x2, v);
+      r[2 * t] = w[0];
+      r[2 * t + 1] = w[1];
+    }
+    return r;
+  }
+
+  // FIRST: the first K slice, whose MFMAs start from an accumulator of 0
+  // (an inline constant), so the accumulators are never written by VALU code.
+  template <bool FIRST>
+  __device__ static __forceinline__ Acc mma(const Frag &x, const Frag &y, const Acc &c, int sx, int sy) {
+    // The 16 x 16 forms are written as inline asm with the accumulator tied
+    // in place ("+a"): with the builtin the register allocator rotates the
+    // 64 accumulator tuples through spare registers on every loop trip.  The
+    // compiler still places the LDS waits for the fragment inputs; the
+    // accumulators are never written by VALU code and are read by it only
+    // after fence_acc().
     if constexpr (KIND == 0) {
-      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y),
-                                                     c, 0, 0, 0);
+      Acc d = c;
+      if constexpr (FIRST)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(d) : "v"(x), "v"(y));
+      else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
+      return d;
     } else if constexpr (KIND == 1) {
-      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
-                                                    0, 0, 0);
+      Acc d = c;
+      if constexpr (FIRST)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(d) : "v"(x), "v"(y));
+      else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
+      return d;
     } else {
       // Format code 0 (OCP FP8 E4M3) for both operands; byte 0 of each scale VGPR.
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, sx, 0, sy);
     }
   }
 
-  // Fragments of one K substep: x = 4 blocks of B rows, y = 4 blocks of A rows.
-  struct Frags {
-    Frag x[4], y[4];
-  };
+  // Wait states after the last MFMA before VALU code reads the
+  // accumulators.  The empty asm statements redefine every accumulator after
+  // the s_nops, so no accumulator read can be scheduled above them.
+  __device__ __forceinline__ void fence_acc() {
+    mfma_fence();
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
 
-  // Fragment read q (0..7) of substep `sub` of slot S, in order of first use
-  // by the MFMA sequence (x[0] with y[0..3], then x[1], x[2], x[3]):
-  // q = 0 -> x[0], 1..4 -> y[0..3], 5..7 -> x[1..3].
-  template <int S>
-  __device__ __forceinline__ void read_one(Frags &f, int sub, int q) const {
-    if (q >= 1 && q <= 4) {
-      const int j = q - 1;
-      f.y[j] = read_frag(slots.a[S], wave_m * 128 + j * 32 + (lane & 31), sub);
+  // Fragment read R (0 .. 2 kNB - 1) of slot S, in an order that lets the
+  // reads reuse the registers of fragments already consumed: the first half
+  // of the x blocks, then all y blocks, then the second half of x.
+  template <int S, int R>
+  __device__ __forceinline__ void read_one(Frags &f) const {
+    constexpr int H = kNB / 2;
+    if constexpr (R < H || R >= H + kNB) {
+      constexpr int i = R < H ? R : R - kNB;
+      if constexpr (T::kNN)
+        f.x[i] = read_cols(slots.b[S], wave_n * 128 + i * kBlk);
+      else
+        f.x[i] = read_rows(slots.b[S], wave_n * 128 + i * kBlk);
     } else {
-      const int i = q == 0 ? 0 : q - 4;
-      f.x[i] = read_frag(slots.b[S], wave_n * 128 + i * 32 + (lane & 31), sub);
+      constexpr int j = R - H;
+      f.y[j] = read_rows(slots.a[S], wave_m * 128 + j * kBlk);
     }
   }
 
-  // Load instruction q (0..15) of slice kt into slot S: 8 A-panel DMAs, then
-  // the B side (8 DMAs for NT, 8 row loads into registers for NN).
+  // Load instruction i (0..7) of slice kt into slot S: A panel, then B.
   template <int S>
-  __device__ __forceinline__ void load_one(int kt, const PanelLoader::Slice &sa, const PanelLoader::Slice &sb,
-                                           int q) {
-    if (q < 8) {
-      la.issue_one(slots.a[S], wave, sa, q);
+  __device__ __forceinline__ void load_one(int kt, int i) {
+    if (i < 4) {
+      la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
     } else if constexpr (T::kNN) {
-      lnn.load_one(kt, a.K, q - 8);
+      lnn.issue(slots.b[S], wave, kt, a.K, i - 4);
     } else {
-      lb.issue_one(slots.b[S], wave, sb, q - 8);
+      lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - 4);
     }
   }
 
-  template <int S>
+  // Scale bytes of slice kt into set P (a slice is half a 128-element
+  // scale block).
+  template <int P>
   __device__ __forceinline__ void load_scales(int kt) {
     if constexpr (T::kScaled) {
       const bool ok = kt < nk;
+      const uint32_t blk = (uint32_t)(kt >> 1);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        sc[S][b] = __builtin_amdgcn_raw_buffer_load_b8(rsb, ok ? soB[b] + (uint32_t)kt : kOOB, 0, 0);
-        sc[S][4 + b] = __builtin_amdgcn_raw_buffer_load_b8(rsa, ok ? soA[b] + (uint32_t)kt : kOOB, 0, 0);
+        sc[P][b] = __builtin_amdgcn_raw_buffer_load_b8(rsb, ok ? soB[b] + blk : kOOB, 0, 0);
+        sc[P][4 + b] = __builtin_amdgcn_raw_buffer_load_b8(rsa, ok ? soA[b] + blk : kOOB, 0, 0);
       }
     }
   }
 
-  // The 16 MFMAs of one substep on fragments `f` with the scales of slot S,
-  // interleaved with 8 fragment reads into `nf` (slot RS, substep rsub) and,
-  // if LOAD, the 16 load instructions of slice lkt into slot LS.
-  template <int S, int RS, int LS, bool LOAD>
-  __device__ __forceinline__ void mfma16(const Frags &f, Frags &nf, int rsub, int lkt, const PanelLoader::Slice &sa,
-                                         const PanelLoader::Slice &sb) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if constexpr (LOAD) load_one<LS>(lkt, sa, sb, q);
-      if ((q & 1) == 0) read_one<RS>(nf, rsub, q >> 1);
-      const int i = q >> 2, j = q & 3;
-      acc[i][j] = mma(f.x[i], f.y[j], acc[i][j], sc[S][i], sc[S][4 + j]);
-      __builtin_amdgcn_sched_barrier(0);
+  // MFMA Q of the slice held in slot S (x block Q / kNB times y block
+  // Q % kNB), with scale set P.  Every kMfma / 8 MFMAs one load instruction
+  // of slice kt + 3 goes out; in the second half, one fragment read of the
+  // next slot (slot NX) per MFMA into `nf`.
+  template <int S, int P, bool FIRST, int Q>
+  __device__ __forceinline__ void mfma_one(int kt, const Frags &f, Frags &nf) {
+    constexpr int I = Q / kNB, J = Q % kNB;
+    constexpr int kEvery = kMfma / kLoads;
+    constexpr int L = (S + kAhead) & 3, NX = (S + 1) & 3;
+    if constexpr (Q >= kHalf && Q - kHalf < 2 * kNB) read_one<NX, Q - kHalf>(nf);
+    if constexpr (Q % kEvery == kEvery / 2) load_one<L>(kt + kAhead, Q / kEvery);
+    if constexpr (T::kScaled)
+      acc[I][J] = mma<FIRST>(f.x[I], f.y[J], acc[I][J], sc[P][I], sc[P][4 + J]);
+    else
+      acc[I][J] = mma<FIRST>(f.x[I], f.y[J], acc[I][J], 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (Q == kHalf - 1) {
+      // Slice kt + 1 has landed in slot NX for this wave; once every wave
+      // is here it is visible to all, and no wave still reads the slot the
+      // next loads will overwrite.
+      wait_vm_lgkm0<kWaitVm>();
+      barrier();
     }
   }
 
-  // One K step on slot S (slice kt), entered with substep 0's fragments in
-  // f0.  The loads of slice kt + 1 into the other slot go out during
-  // substep 0.  Before the last substep the wave waits for them and the
-  // workgroup synchronises, so the last substep's MFMAs overlap the first
-  // fragment reads of slice kt + 1.
-  template <int S>
-  __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
-    const auto sa = la.slice(kt + 1, a.K, kSliceK);
-    const auto sb = lb.slice(kt + 1, a.K, kSliceK);
-    load_scales<S ^ 1>(kt + 1);
-    if constexpr (kSubsteps == 4) {
-      mfma16<S, S, S ^ 1, true>(f0, f1, 1, kt + 1, sa, sb);
-      mfma16<S, S, S ^ 1, false>(f1, f0, 2, kt + 1, sa, sb);
-      mfma16<S, S, S ^ 1, false>(f0, f1, 3, kt + 1, sa, sb);
-    } else {
-      mfma16<S, S, S ^ 1, true>(f0, f1, 1, kt + 1, sa, sb);
-    }
-    if constexpr (T::kNN) lnn.store(slots.b[S ^ 1], tid);
-    wait_vm0_lgkm0();
-    barrier();
-    mfma16<S, S ^ 1, S ^ 1, false>(f1, f0, 0, kt + 1, sa, sb);
+  template <int S, int P, bool FIRST, int... Q>
+  __device__ __forceinline__ void slice_seq(std::integer_sequence<int, Q...>, int kt, const Frags &f, Frags &nf) {
+    (mfma_one<S, P, FIRST, Q>(kt, f, nf), ...);
+  }
+
+  // One K slice kt from slot S (its fragments already in `f`).
+  template <int S, bool FIRST = false>
+  __device__ __forceinline__ void step(int kt, const Frags &f, Frags &nf) {
+    constexpr int P = S & 1;
+    load_scales<P ^ 1>(kt + 1);
+    slice_seq<S, P, FIRST>(std::make_integer_sequence<int, kMfma>(), kt, f, nf);
+  }
+
+  template <int S, int... R>
+  __device__ __forceinline__ void read_all(std::integer_sequence<int, R...>, Frags &f) const {
+    (read_one<S, R>(f), ...);
   }
 
   __device__ __forceinline__ void run() {
@@ -376,8 +458,7 @@ struct Kernel {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     wave_m = wave >> 1;
     wave_n = wave & 1;
-    hi = lane >> 5;
-    lane_sw = swz(lane & 31);  // fragment blocks start at multiples of 32 rows
+    lane_sw = swz(lane & 15);  // fragment blocks start at multiples of 16 rows
 
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -388,7 +469,7 @@ struct Kernel {
 
     la.init(a.A + (size_t)m0 * K * kElem, min(a.M - m0, kTileM), K, kElem, wave, lane);
     if constexpr (T::kNN)
-      lnn.init(a.B, K, a.N, n0, tid);
+      lnn.init(a.B, K, a.N, n0, wave, lane);
     else
       lb.init(a.B + (size_t)n0 * K * kElem, min(a.N - n0, kTileN), K, kElem, wave, lane);
     if constexpr (T::kScaled) {
@@ -406,52 +487,65 @@ struct Kernel {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc[s][b] = 0;
+    if constexpr (T::kScaled) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    if (nk > 0) {
-      {
-        const auto sa = la.slice(0, K, kSliceK);
-        const auto sb = lb.slice(0, K, kSliceK);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) load_one<0>(0, sa, sb, q);
-        load_scales<0>(0);
-        if constexpr (T::kNN) lnn.store(slots.b[0], tid);
-        wait_vm0_lgkm0();
-        barrier();
-      }
-      Frags f0, f1;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) read_one<0>(f0, 0, q);
-      // Slices are taken in pairs; with an odd count the last pair's second
-      // slice is all zeros.
-      for (int kt = 0; kt < nk; kt += 2) {
-        step<0>(kt, f0, f1);
-        step<1>(kt + 1, f0, f1);
-      }
+        for (int j = 0; j < kNB; ++j) acc[i][j] = Acc{};
     }
+
+    // Prologue: slices 0 .. 2 into slots 0 .. 2 and the scales of slice 0;
+    // wait for slice 0.  (With K = 0 every slice is all zeros.)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_one<0>(0, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_one<1>(1, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_one<2>(2, i);
+    load_scales<0>(0);
+    wait_vm_lgkm0<2 * kLoads>();
+    barrier();
+    Frags f0, f1;
+    read_all<0>(std::make_integer_sequence<int, 2 * kNB>(), f0);
+    // Slice 0 starts the accumulators; then slices go four at a time, one
+    // per slot.  The count is padded: slices past nk arrive as zeros and add
+    // nothing.  (Leaving the loop early instead makes the register allocator
+    // copy the accumulators around and spill.)
+    step<0, true>(0, f0, f1);
+    for (int kt = 0; kt + 1 < nk; kt += 4) {
+      step<1>(kt + 1, f1, f0);
+      step<2>(kt + 2, f0, f1);
+      step<3>(kt + 3, f1, f0);
+      step<0>(kt + 4, f0, f1);
+    }
+    // Drain the loads still in flight into the ring before the workgroup
+    // can finish.
+    wait_vm_lgkm0<0>();
+    fence_acc();
     epilogue();
   }
 
-  // acc[i][j] covers B rows (C columns) n0 + 128 wave_n + 32 i and A rows
-  // (C rows) m0 + 128 wave_m + 32 j.  Lane l, register r holds C row l % 32
-  // of the block, column 8 (r / 4) + 4 (l / 32) + r % 4.
+  // acc[i][j] covers B rows (C columns) n0 + 128 wave_n + kBlk i and A rows
+  // (C rows) m0 + 128 wave_m + kBlk j.  32 x 32 blocks: lane l, register r
+  // holds C row l % 32 of the block, column 8 (r / 4) + 4 (l / 32) + r % 4.
+  // 16 x 16 blocks: lane l, register r holds row l % 16, column
+  // 4 (l / 16) + r.  Either way four consecutive columns leave as one
+  // 8-byte store.
   __device__ __forceinline__ void epilogue() {
-    const int row_l = lane & 31;
+    constexpr int kRowLanes = kBlk;          // lanes l % kBlk index the row
+    constexpr int kGroups = kBlk == 32 ? 4 : 1;
+    const int row_l = lane % kRowLanes;
+    const int colq = kBlk == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wave_m * 128 + j * 32 + row_l;
+    for (int j = 0; j < kNB; ++j) {
+      const int m = m0 + wave_m * 128 + j * kBlk + row_l;
       if (m >= a.M) continue;
       uint8_t *crow = a.C + (size_t)m * a.N * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kNB; ++i) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wave_n * 128 + i * 32 + g * 8 + hi * 4;
+        for (int g = 0; g < kGroups; ++g) {
+          const int n = n0 + wave_n * 128 + i * kBlk + g * 8 + colq;
           if (n >= a.N) continue;
           const f32x2 lo = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]};
           const f32x2 up = {acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
@@ -472,18 +566,26 @@ struct Kernel {
 
 template <int KIND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(const Args a) {
+  // Eight separate arrays (not one indexed array) so the compiler can tell
+  // the slot being loaded from the slot being read and does not insert a
+  // vmcnt wait in front of every LDS read.
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA3[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB3[kSlotBytes];
   Slots slots;
   slots.a[0] = (LDS_AS uint8_t *)sA0;
   slots.a[1] = (LDS_AS uint8_t *)sA1;
+  slots.a[2] = (LDS_AS uint8_t *)sA2;
+  slots.a[3] = (LDS_AS uint8_t *)sA3;
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
-  // An AGPR operand in inline asm keeps AGPR allocation enabled for this
-  // kernel, so the MFMAs accumulate in AGPRs instead of spilling VGPRs.
-  asm volatile("; agpr %0" ::"a"(0));
+  slots.b[2] = (LDS_AS uint8_t *)sB2;
+  slots.b[3] = (LDS_AS uint8_t *)sB3;
   Kernel<KIND> k(a, slots);
   k.run();
 }
@@ -502,7 +604,7 @@ hipError_t launch(const Problem &p) {
   a.K = (int)p.K;
   a.tiles_m = (int)((p.M + kTileM - 1) / kTileM);
   a.tiles_n = (int)((p.N + kTileN - 1) / kTileN);
-  const int slice = p.kind == Kind::kMxfp8NT ? 128 : 64;
+  const int slice = p.kind == Kind::kMxfp8NT ? 64 : 32;
   a.ksteps = (int)((p.K + slice - 1) / slice);
   a.kb = (int)((p.K + 127) / 128);
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
