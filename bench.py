@@ -12,14 +12,30 @@ goes to stderr.
 
 The line carries:
   roofline     the kernel against MI355X's dense bf16 MFMA peak: algorithmic
-               flops per launch over the kernel's mean duration, measured
-               with HIP events recorded around single launches on the stream
-               the kernel runs on; `traffic` is the HBM bytes per launch from
-               rocprofv3 FETCH_SIZE/WRITE_SIZE counters when a committed
-               measurement matches the current kernel source, else null;
+               flops per launch over the kernel's mean duration, taken from
+               the HIP events that bracket the timed region on the stream the
+               kernel runs on (one kernel per step, launched back to back);
+               `traffic` is the HBM bytes per launch from rocprofv3
+               FETCH_SIZE/WRITE_SIZE counters, calibrated on a plain copy,
+               when a committed measurement matches the current kernel
+               source, else null;
   cpu_baseline the CPU oracle (binary64 triple loop, all host threads) timed
                on a bounded sample of the same workload: whole rows of C,
                scaled to TFLOPS.
+
+The MI355X holds its board power cap under this load and its clock settles
+over about a second, so the default warmup is long (about 2 s of launches).
+
+Two helper modes serve the traffic measurement:
+  --copy-calibration       only run a plain device-to-device copy of 1 GiB
+                           (torch's copy kernel) a few times, for rocprofv3
+                           to count what a copy of known size reads/writes;
+  --record-traffic DIR     host only: read the four rocprofv3 --pmc CSVs in
+                           DIR (gemm_fetch, gemm_write, copy_fetch,
+                           copy_write), scale the GEMM's per-dispatch
+                           FETCH_SIZE and WRITE_SIZE by the copy's ratio of
+                           known bytes to counted bytes, and write the JSON
+                           record bench.py reads plus a short summary.
 """
 from __future__ import annotations
 
@@ -150,16 +166,90 @@ def cpu_baseline(w, x, target_s: float):
             "seconds": t}
 
 
+COPY_REPS = 5
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain copy of known size: reads and writes COPY_BYTES per dispatch."""
+    import torch
+    torch.cuda.set_device(0)
+    n = COPY_BYTES
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {n} bytes x {COPY_REPS}")
+
+
+def _counter_per_dispatch(path: str, counter: str, match):
+    import csv
+    per = {}
+    names = set()
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
+            continue
+        per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        names.add(r["Kernel_Name"])
+    if not per:
+        raise SystemExit(f"{path}: no {counter} records for the kernel")
+    vals = sorted(per.values())
+    return sum(vals) / len(vals), len(vals), sorted(names)
+
+
+def record_traffic(d: str, name: str):
+    """Per-launch HBM bytes of the GEMM from FETCH_SIZE/WRITE_SIZE (KiB per
+    dispatch), each scaled by known bytes / counted bytes of a plain copy."""
+    import workloads
+    w = workloads.WORKLOADS[name]
+    f = lambda stem: os.path.join(d, f"{stem}_counter_collection.csv")
+    is_gemm = lambda k: "gemm_kernel" in k
+    is_copy = lambda k: "copy" in k.lower()
+    g_fetch, nd_f, gnames = _counter_per_dispatch(f("gemm_fetch"), "FETCH_SIZE", is_gemm)
+    g_write, nd_w, _ = _counter_per_dispatch(f("gemm_write"), "WRITE_SIZE", is_gemm)
+    c_fetch, _, cnames = _counter_per_dispatch(f("copy_fetch"), "FETCH_SIZE", is_copy)
+    c_write, _, _ = _counter_per_dispatch(f("copy_write"), "WRITE_SIZE", is_copy)
+    copy_bytes = COPY_BYTES
+    kf = copy_bytes / (c_fetch * 1024.0)
+    kw = copy_bytes / (c_write * 1024.0)
+    fetch_b = g_fetch * 1024.0 * kf
+    write_b = g_write * 1024.0 * kw
+    out_elem = 2
+    in_bytes = w.M * w.K * (1 if w.kind == "mxfp8_nt" else 2) + w.N * w.K * (1 if w.kind == "mxfp8_nt" else 2)
+    alg = in_bytes + w.M * w.N * out_elem
+    rec = {"workload": name, "kernel_source_sha256_16": kernel_source_hash(),
+           "kernel": gnames, "dispatches": [nd_f, nd_w],
+           "fetch_kib_per_dispatch": round(g_fetch, 1), "write_kib_per_dispatch": round(g_write, 1),
+           "copy_kernel": cnames, "copy_bytes": copy_bytes,
+           "copy_fetch_kib": round(c_fetch, 1), "copy_write_kib": round(c_write, 1),
+           "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
+           "hbm_read_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
+           "hbm_bytes_per_launch": int(fetch_b + write_b),
+           "algorithmic_bytes_per_launch": alg,
+           "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 3)}
+    out = os.path.join(d, f"traffic_{name}.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=10000)
+    ap.add_argument("--warmup", type=int, default=10000)
     ap.add_argument("--workload", default="bf16_nt_4096x4096x8192")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work for the oracle baseline (0 disables it)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--record-traffic", metavar="DIR")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.workload)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; --gpus must be 1 "
@@ -169,6 +259,10 @@ def main():
     import torch
     import dense_tiled_gemm_bf16_amd as tg
     import workloads
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     w = workloads.WORKLOADS[args.workload]
     prec = {"bf16_nt": "bf16", "f16_nn": "f16", "mxfp8_nt": "mxfp8"}[w.kind]
@@ -203,23 +297,13 @@ def main():
     ms_per_step = total_ms / args.steps
     tflops = w.flops * args.steps / (total_ms / 1e3) / 1e12
 
-    # Kernel duration: event pairs around single launches on the kernel's stream.
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(max(10, min(args.steps, 50)))]
-    with torch.cuda.stream(stream):
-        for e0, e1 in pairs:
-            e0.record(stream)
-            launch()
-            e1.record(stream)
-    torch.cuda.synchronize()
-    durs = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
-    kernel_ms = sum(durs) / len(durs)
+    # One kernel per step, launched back to back on `stream`: the kernel's
+    # mean duration is the event-timed region over the step count.
+    kernel_ms = ms_per_step
     achieved = w.flops / (kernel_ms / 1e3) / 1e12
     peak = PEAK_TFLOPS[prec]
     log(f"[bench] {args.steps} steps in {total_ms:.3f} ms (wall {wall*1e3:.1f} ms): "
         f"{ms_per_step*1e3:.1f} us/step, {tflops:.1f} TFLOPS = {100*tflops/peak:.1f}% of {peak}")
-    log(f"[bench] kernel mean {kernel_ms*1e3:.1f} us (min {durs[0]*1e3:.1f}, max {durs[-1]*1e3:.1f}) "
-        f"-> {achieved:.1f} TFLOPS, {100*achieved/peak:.1f}% of peak")
 
     parity = None if args.no_parity else parity_sample(w, x, out)
     if parity is not None:
