@@ -24,11 +24,12 @@
 //  * pipelined K loop: the pages use a 3-slot ring with producer and
 //    consumer warpgroups and mbarrier parity waits (velog "tilelang",
 //    Device IRModule).  Here every wave both loads and computes, with two
-//    slots: once three quarters of slice kt's MFMAs are issued, a wait and a
-//    barrier free slot kt % 2; the loads of slice kt + 2 into it then go out
-//    one per four MFMAs over the next half slice, and have another half
-//    slice to land before they are needed.  The next slice's first operand
-//    reads overlap the current slice's last quarter.
+//    slots: partway through slice kt's MFMAs (halfway for 16-bit inputs,
+//    three quarters for fp8) a wait and a barrier free slot kt % 2; the
+//    loads of slice kt + 2 into it then go out spread over the next half
+//    slice of MFMAs and have at least another half slice to land before
+//    they are needed.  The next slice's first operand reads follow the
+//    barrier, overlapping the current slice's remaining MFMAs.
 //  * wave-tile MMA: v_mfma_f32_16x16x32_{bf16,f16} (8 x 8 blocks per wave)
 //    and, for the block-scaled path, v_mfma_scale_f32_32x32x64_f8f6f4
 //    (4 x 4 blocks) with the e8m0 block scales as operands (TCGEN05
