@@ -236,6 +236,7 @@ struct NNLoader {
 struct Slots {
   LDS_AS uint8_t *a[2];
   LDS_AS uint8_t *b[2];
+  LDS_AS uint8_t *junk;  // 256 bytes per wave: landing area of the L2 prefetches
 };
 
 template <int KIND>
@@ -248,7 +249,8 @@ struct Kernel {
   // the 32 x 32 x 16 form; under full load the chip is power-capped, and the
   // lower-energy form runs at a higher clock).  fp8: the scaled 32 x 32 x 64
   // form.  Either way a slice is two K substeps.
-  static constexpr int kBlk = T::kScaled ? 32 : 16;
+  static constexpr bool kW = T::kScaled;        // 32 x 32 blocks
+  static constexpr int kBlk = kW ? 32 : 16;
   static constexpr int kNB = 128 / kBlk;        // blocks per wave along M and along N
   static constexpr int kPerSub = kNB * kNB;     // MFMAs per substep
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
@@ -265,6 +267,25 @@ struct Kernel {
   static constexpr int kWindow = kMfma / 2;
   static_assert(kBarrierAt + 2 * kNB <= kMfma, "next-slice fragment reads must fit after the barrier");
   static_assert(kWindow <= kMfma && kWindow >= kLoads, "load window");
+
+  // L2 prefetch (fp8 only).  A slice's lines are first touched by its loads
+  // into LDS, which have about one slice to land.  For fp8, whose slices
+  // hold twice the flops of the 16-bit kinds' 64-element slices but whose
+  // loads are half issued in the slice before the barrier that waits for
+  // them, one dword of every 128-byte line of slice kt + kPfDist is loaded
+  // early (into a scratch LDS area, no registers), right after the last LDS
+  // load that the next barrier waits for: that barrier waits with
+  // vmcnt(1), and the prefetch has until the barrier after it, about 1.5
+  // slices, to complete -- before the LDS loads of slice kt + kPfDist are
+  // issued.  The workgroups of an XCD that share a panel split its lines
+  // between them.  Measured: 7% fewer cycles for fp8; none for the 16-bit
+  // kinds, which do not use it.
+  static constexpr int kLastLoad = kBarrierAt + (kLoads - 1) * kWindow / kLoads;
+  static constexpr bool kPfHead = kLastLoad >= kMfma;  // last load in the next slice's head
+  static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
+  static constexpr int kPfDist = T::kScaled ? 3 : 0;
+  static_assert(!kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
+  static_assert(kPfHead || kPfAt < kMfma, "prefetch position");
 
   // Loads of a slice issued in the tail of the slice two before it.
   static constexpr int tail_loads() {
@@ -285,8 +306,8 @@ struct Kernel {
     return -1;
   }
 
-  using Frag = typename std::conditional<T::kScaled, i32x8, u32x4>::type;
-  using Acc = typename std::conditional<T::kScaled, f32x16, f32x4>::type;
+  using Frag = typename std::conditional<kW, i32x8, u32x4>::type;
+  using Acc = typename std::conditional<kW, f32x16, f32x4>::type;
   struct Frags {
     Frag x[kNB], y[kNB];
   };
@@ -298,6 +319,8 @@ struct Kernel {
   int nk;
   PanelLoader la, lb;
   NNLoader lnn;
+  __amdgpu_buffer_rsrc_t pf_rsrc;
+  uint32_t pf_off;
   __amdgpu_buffer_rsrc_t rsa, rsb;
   uint32_t soA[4], soB[4];
   // Scale bytes by slice parity: the B-row scales of the 4 x blocks, then the
@@ -310,7 +333,7 @@ struct Kernel {
   // Fragment of one block of kBlk rows (B rows = C columns for x, A rows for
   // y), K substep `sub`, from a K-contiguous slot.
   __device__ __forceinline__ Frag read_rows(const LDS_AS uint8_t *slot, int row0, int sub) const {
-    if constexpr (T::kScaled) {
+    if constexpr (kW) {
       // 32 x 32 x 64: lane l holds row l % 32 and 32 bytes of K: logical
       // chunks 4 sub + 2 (l / 32) and the one after.
       const int c = 4 * sub + 2 * (lane >> 5);
@@ -424,6 +447,14 @@ struct Kernel {
     }
   }
 
+  // One dword of each 128-byte line of slice kt of this workgroup's share of
+  // the A and B panels; out-of-range rows and slices past K load nothing.
+  __device__ __forceinline__ void prefetch(int kt) {
+    const bool ok = kt * kSliceK < a.K;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (LDS_AS void *)(slots.junk + wave * 256), 4,
+                                             ok ? pf_off : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
+  }
+
   // Scale bytes of slice kt (one 128-element scale block) into set P.
   template <int P>
   __device__ __forceinline__ void load_scales(int kt) {
@@ -451,13 +482,17 @@ struct Kernel {
     constexpr int I = q / kNB, J = q % kNB;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
     if constexpr (Q == kBarrierAt) {
-      wait_vm_lgkm0<0>();
+      // The prefetch issued after the last needed load may be outstanding
+      // (none precedes the first slice's barrier in the tail placement).
+      constexpr int kPfOut = kPfDist > 0 && (kPfHead || !FIRST) ? 1 : 0;
+      wait_vm_lgkm0<kPfOut>();
       barrier();
     }
     if constexpr (Q < 2 * kNB) read_one<S, Q>(f1, 1);
     if constexpr (Q >= kBarrierAt && Q - kBarrierAt < 2 * kNB) read_one<S ^ 1, Q - kBarrierAt>(f0, 0);
     if constexpr (kHead >= 0) load_one<S ^ 1>(kt + 1, kHead);
     if constexpr (kTail >= 0) load_one<S>(kt + 2, kTail);
+    if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
     const Frags &f = SUB == 0 ? f0 : f1;
     if constexpr (T::kScaled)
       acc[I][J] = mma<FIRST && SUB == 0>(f.x[I], f.y[J], acc[I][J], sc[P][I], sc[P][4 + J]);
@@ -499,6 +534,17 @@ struct Kernel {
       lnn.init(a.B, K, a.N, n0, wave, lane);
     else
       lb.init(a.B + (size_t)n0 * K * kElem, min(a.N - n0, kTileN), K, kElem, wave, lane);
+    if constexpr (kPfDist > 0) {
+      // Waves 0-1 take 32 rows of the A panel (its share among the 8 tile
+      // columns of an XCD's block), waves 2-3 take 64 rows of the B panel
+      // (its share among the 4 tile rows).
+      const bool is_a = wave < 2;
+      pf_rsrc = is_a ? la.rsrc : lb.rsrc;
+      const int rows_valid = is_a ? min(a.M - m0, kTileM) : min(a.N - n0, kTileN);
+      const int r = is_a ? 32 * (tn & 7) + 16 * wave + (lane & 15) : 64 * (tm & 3) + 32 * (wave - 2) + (lane & 31);
+      const bool active = is_a ? lane < 16 : lane < 32;
+      pf_off = active && r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)kElem : kOOB;
+    }
     if constexpr (T::kScaled) {
       rsa = make_rsrc(a.SA, (uint32_t)a.M * (uint32_t)a.kb);
       rsb = make_rsrc(a.SB, (uint32_t)a.N * (uint32_t)a.kb);
@@ -595,11 +641,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[kSlotBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t junk[4 * 256];
   Slots slots;
   slots.a[0] = (LDS_AS uint8_t *)sA0;
   slots.a[1] = (LDS_AS uint8_t *)sA1;
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
+  slots.junk = (LDS_AS uint8_t *)junk;
   Kernel<KIND> k(a, slots);
   k.run();
 }
