@@ -321,11 +321,18 @@ struct Kernel {
   NNLoader lnn;
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
-  __amdgpu_buffer_rsrc_t rsa, rsb;
-  uint32_t soA[4], soB[4];
-  // Scale bytes by slice parity: the B-row scales of the 4 x blocks, then the
-  // A-row scales of the 4 y blocks (each in byte 0 of its register).
-  int sc[2][8];
+  // Block scales (fp8).  They are fetched once per group of 4 slices: a
+  // row's scale bytes for slices 4 g .. 4 g + 3 are consecutive, so each
+  // lane loads the two aligned dwords that hold them for one of 64 rows
+  // (instruction j: the wave's B rows 64 j .. + 63 for j < 2, its A rows
+  // 64 (j - 2) .. + 63 after), shifts them into one dword and hands it to
+  // the lanes that feed that row to the MFMA.  The MFMA's byte select then
+  // picks the slice, so no per-slice work remains.
+  __amdgpu_buffer_rsrc_t rss[2];  // B scales, A scales; based at the tile's first row, dword aligned
+  uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
+  uint32_t sc_sh[4];              // per instruction: byte shift of the row inside that dword pair
+  uint32_t sc_raw[4][2];          // the next group, in flight
+  int sc_nxt[8], sc_cur[8];       // per block (4 x blocks, then 4 y blocks): bytes of 4 slices
   Acc acc[kNB][kNB];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
@@ -377,7 +384,7 @@ struct Kernel {
 
   // FIRST: the first K substep, whose MFMAs start from an accumulator of 0
   // (an inline constant), so the accumulators are never written by VALU code.
-  template <bool FIRST>
+  template <bool FIRST, int JB = 0>
   __device__ static __forceinline__ Acc mma(const Frag &x, const Frag &y, const Acc &c, int sx, int sy) {
     // The 16 x 16 forms are written as inline asm with the accumulator tied
     // in place ("+a"): with the builtin the register allocator rotates the
@@ -400,8 +407,9 @@ struct Kernel {
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
       return d;
     } else {
-      // Format code 0 (OCP FP8 E4M3) for both operands; byte 0 of each scale VGPR.
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, sx, 0, sy);
+      // Format code 0 (OCP FP8 E4M3) for both operands; byte JB of each
+      // scale VGPR (the slice's place in its group of 4).
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, JB, sx, JB, sy);
     }
   }
 
@@ -455,16 +463,26 @@ struct Kernel {
                                              ok ? pf_off : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
   }
 
-  // Scale bytes of slice kt (one 128-element scale block) into set P.
-  template <int P>
-  __device__ __forceinline__ void load_scales(int kt) {
-    if constexpr (T::kScaled) {
-      const bool ok = kt < nk;
+  // Scale dwords of group g (slices 4 g .. 4 g + 3); a group past the last
+  // scale block loads nothing (its slices are all zeros).
+  __device__ __forceinline__ void load_scale_group(int g) {
+    const bool ok = 4 * g < a.kb;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        sc[P][b] = __builtin_amdgcn_raw_buffer_load_b8(rsb, ok ? soB[b] + (uint32_t)kt : kOOB, 0, 0);
-        sc[P][4 + b] = __builtin_amdgcn_raw_buffer_load_b8(rsa, ok ? soA[b] + (uint32_t)kt : kOOB, 0, 0);
-      }
+    for (int j = 0; j < 4; ++j) {
+      sc_raw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rss[j >> 1], ok ? sc_off[j] : kOOB, 4u * g, 0);
+      sc_raw[j][1] = __builtin_amdgcn_raw_buffer_load_b32(rss[j >> 1], ok ? sc_off[j] + 4 : kOOB, 4u * g, 0);
+    }
+  }
+
+  // The loaded group, shifted and redistributed: block 2 j + h of
+  // instruction j's rows is rows 32 h .. 32 h + 31, which lane l (both
+  // halves of the wave) takes from lane 32 h + l % 32.
+  __device__ __forceinline__ void convert_scales() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = (int)__builtin_amdgcn_alignbyte(sc_raw[j][1], sc_raw[j][0], sc_sh[j]);
+      sc_nxt[2 * j] = __builtin_amdgcn_ds_bpermute((lane & 31) << 2, d);
+      sc_nxt[2 * j + 1] = __builtin_amdgcn_ds_bpermute((32 + (lane & 31)) << 2, d);
     }
   }
 
@@ -476,7 +494,7 @@ struct Kernel {
   //  * from kBarrierAt: reads of substep 0 of slice kt + 1 into f0;
   //  * the loads of slice kt + 2 into this slot, and the end of those of
   //    slice kt + 1 into the other slot, as load_at places them.
-  template <int S, int P, bool FIRST, int Q>
+  template <int S, int JB, bool FIRST, int Q>
   __device__ __forceinline__ void mfma_one(int kt, Frags &f0, Frags &f1) {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
     constexpr int I = q / kNB, J = q % kNB;
@@ -487,6 +505,8 @@ struct Kernel {
       constexpr int kPfOut = kPfDist > 0 && (kPfHead || !FIRST) ? 1 : 0;
       wait_vm_lgkm0<kPfOut>();
       barrier();
+      // Scales of the next group: waited for by the next slice's barrier.
+      if constexpr (T::kScaled && JB == 1) load_scale_group((kt + 3) >> 2);
     }
     if constexpr (Q < 2 * kNB) read_one<S, Q>(f1, 1);
     if constexpr (Q >= kBarrierAt && Q - kBarrierAt < 2 * kNB) read_one<S ^ 1, Q - kBarrierAt>(f0, 0);
@@ -495,23 +515,27 @@ struct Kernel {
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
     const Frags &f = SUB == 0 ? f0 : f1;
     if constexpr (T::kScaled)
-      acc[I][J] = mma<FIRST && SUB == 0>(f.x[I], f.y[J], acc[I][J], sc[P][I], sc[P][4 + J]);
+      acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
       acc[I][J] = mma<FIRST && SUB == 0>(f.x[I], f.y[J], acc[I][J], 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  template <int S, int P, bool FIRST, int... Q>
+  template <int S, int JB, bool FIRST, int... Q>
   __device__ __forceinline__ void slice_seq(std::integer_sequence<int, Q...>, int kt, Frags &f0, Frags &f1) {
-    (mfma_one<S, P, FIRST, Q>(kt, f0, f1), ...);
+    (mfma_one<S, JB, FIRST, Q>(kt, f0, f1), ...);
   }
 
-  // One K slice kt from slot S (its substep-0 fragments already in f0).
-  template <int S, bool FIRST = false>
+  // One K slice kt from slot S (its substep-0 fragments already in f0); JB
+  // = kt % 4 for the block-scaled kind.
+  template <int S, int JB, bool FIRST = false>
   __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
-    constexpr int P = S;  // scale set by slice parity
-    load_scales<P ^ 1>(kt + 1);
-    slice_seq<S, P, FIRST>(std::make_integer_sequence<int, kMfma>(), kt, f0, f1);
+    if constexpr (T::kScaled && JB == 3) convert_scales();  // the group loaded in slice kt - 2
+    if constexpr (T::kScaled && JB == 0 && !FIRST) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
+    }
+    slice_seq<S, JB, FIRST>(std::make_integer_sequence<int, kMfma>(), kt, f0, f1);
   }
 
   __device__ __forceinline__ void run() {
@@ -546,46 +570,66 @@ struct Kernel {
       pf_off = active && r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)kElem : kOOB;
     }
     if constexpr (T::kScaled) {
-      rsa = make_rsrc(a.SA, (uint32_t)a.M * (uint32_t)a.kb);
-      rsb = make_rsrc(a.SB, (uint32_t)a.N * (uint32_t)a.kb);
+      // Each operand's scale rows of this tile through a resource based at
+      // the dword holding its first byte; its size is rounded up to whole
+      // dwords (the extra bytes lie in the same dword as the last scale
+      // byte, so in the same page).
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int m = m0 + wave_m * 128 + b * 32 + (lane & 31);
-        const int n = n0 + wave_n * 128 + b * 32 + (lane & 31);
-        soA[b] = m < a.M ? (uint32_t)m * (uint32_t)a.kb : kOOB;
-        soB[b] = n < a.N ? (uint32_t)n * (uint32_t)a.kb : kOOB;
+      for (int op = 0; op < 2; ++op) {
+        const uintptr_t start = (uintptr_t)(op ? a.SA + (size_t)m0 * a.kb : a.SB + (size_t)n0 * a.kb);
+        const uint32_t mis = (uint32_t)(start & 3);
+        const int rows_valid = op ? min(a.M - m0, kTileM) : min(a.N - n0, kTileN);
+        rss[op] = make_rsrc((const void *)(start - mis), (mis + (uint32_t)rows_valid * (uint32_t)a.kb + 3) & ~3u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j = 2 * op + h;
+          const int r = (op ? wave_m : wave_n) * 128 + 64 * h + lane;
+          const uint32_t pos = mis + (uint32_t)r * (uint32_t)a.kb;
+          sc_off[j] = r < rows_valid ? (pos & ~3u) : kOOB;
+          sc_sh[j] = pos & 3;
+        }
       }
 #pragma unroll
       for (int i = 0; i < kNB; ++i)
 #pragma unroll
         for (int j = 0; j < kNB; ++j) acc[i][j] = Acc{};
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int b = 0; b < 8; ++b) sc[s][b] = 0;
 
-    // Prologue: slice 0 into slot 0, the loads of slice 1 that a previous
-    // slice's tail would have issued, the scales of slice 0; wait for slice 0.
-    // (With K = 0 every slice is all zeros.)
+    // Prologue: the scales of slices 0-3, slice 0 into slot 0, the loads
+    // of slice 1 that a previous slice's tail would have issued; wait for
+    // the first two.  (With K = 0 every slice is all zeros.)
+    if constexpr (T::kScaled) load_scale_group(0);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) load_one<0>(0, i);
     constexpr int kTailLoads = tail_loads();
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) load_one<1>(1, i);
-    load_scales<0>(0);
-    wait_vm_lgkm0<kTailLoads + (T::kScaled ? 8 : 0)>();
+    wait_vm_lgkm0<kTailLoads>();
+    if constexpr (T::kScaled) {
+      convert_scales();
+#pragma unroll
+      for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
+    }
     barrier();
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, 2 * kNB>(), f0, 0);
-    // Slice 0 starts the accumulators; then slices go two at a time, one
-    // per slot.  The count is padded: a slice past nk arrives as zeros and
-    // adds nothing.  (Leaving the loop early instead makes the register
-    // allocator copy the accumulators around and spill.)
-    step<0, true>(0, f0, f1);
-    for (int kt = 1; kt < nk; kt += 2) {
-      step<1>(kt, f0, f1);
-      step<0>(kt + 1, f0, f1);
+    // Slice 0 starts the accumulators; then slices go two (fp8: four) at a
+    // time, alternating slots.  The count is padded: a slice past nk
+    // arrives as zeros and adds nothing.  (Leaving the loop early instead
+    // makes the register allocator copy the accumulators around and spill.)
+    step<0, 0, true>(0, f0, f1);
+    if constexpr (T::kScaled) {
+      for (int kt = 1; kt < nk; kt += 4) {
+        step<1, 1>(kt, f0, f1);
+        step<0, 2>(kt + 1, f0, f1);
+        step<1, 3>(kt + 2, f0, f1);
+        step<0, 0>(kt + 3, f0, f1);
+      }
+    } else {
+      for (int kt = 1; kt < nk; kt += 2) {
+        step<1, 1>(kt, f0, f1);
+        step<0, 2>(kt + 1, f0, f1);
+      }
     }
     // Drain the loads still in flight into the slots before the workgroup
     // can finish.

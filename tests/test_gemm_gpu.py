@@ -198,6 +198,31 @@ def test_mxfp8_per_row_and_per_block_scales_bitwise():
     assert_bitwise(to_bits(run("mxfp8_nt", x, M, N, K)), oracle_full("mxfp8_nt", x), "mxfp8 scales")
 
 
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_mxfp8_unaligned_scale_pointers(offset):
+    """The scale arrays need no alignment: views starting 1-3 bytes into a
+    buffer, with an odd number of scale blocks per row (K = 272, 3 blocks)
+    so that rows start at every byte position of a dword.  Integer elements
+    and per-row, per-block scales: bitwise."""
+    M, N, K = 300, 264, 272
+    x = workloads.make_integer("mxfp8_nt", M, N, K, seed=11 + offset)
+    rng = np.random.default_rng(offset)
+    x["sA"] = rng.integers(124, 131, x["sA"].shape).astype(np.uint8)
+    x["sB"] = rng.integers(124, 131, x["sB"].shape).astype(np.uint8)
+
+    def at_offset(bits):
+        buf = torch.zeros(bits.size + offset, dtype=torch.uint8, device="cuda")
+        buf[offset:] = torch.from_numpy(np.ascontiguousarray(bits).reshape(-1)).cuda()
+        view = buf[offset:].view(bits.shape)
+        assert view.data_ptr() % 4 == offset % 4
+        return view
+
+    print(f"[gpu] mxfp8_nt unaligned scales offset={offset} M={M} N={N} K={K}", flush=True)
+    c = tg.gemm_mxfp8_nt(to_dev(x["qA"], ""), to_dev(x["qB"], ""), at_offset(x["sA"]), at_offset(x["sB"]))
+    torch.cuda.synchronize()
+    assert_bitwise(to_bits(c), oracle_full("mxfp8_nt", x), f"mxfp8 scales at offset {offset}")
+
+
 @pytest.mark.parametrize("kind", ["bf16_nt", "f16_nn", "mxfp8_nt"])
 def test_mid_size_full_parity_several_tiles(kind):
     M, N, K = 776, 520, 1040 if kind != "mxfp8_nt" else 1024
