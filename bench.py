@@ -252,6 +252,8 @@ def main():
                     help="CPU work for the oracle baseline (0 disables it)")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--tile", default="auto",
+                    help="output tile TMxTN (e.g. 256x192); default: the library's own choice")
     ap.add_argument("--record-traffic", metavar="DIR")
     args = ap.parse_args()
 
@@ -276,6 +278,10 @@ def main():
     prec = {"bf16_nt": "bf16", "f16_nn": "f16", "mxfp8_nt": "mxfp8"}[w.kind]
     torch.cuda.set_device(0)
     tg.init()
+    tile = None
+    if args.tile != "auto":
+        tile = tuple(int(v) for v in args.tile.lower().split("x"))
+        tg.set_tile(*tile)
     log(f"[bench] {w.description}: generating inputs")
     x, dev = device_inputs(w)
     out_dtype = torch.float16 if w.kind == "f16_nn" else torch.bfloat16
@@ -340,7 +346,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "layout": "NT" if w.kind != "f16_nn" else "NN",
-                   "accumulate": "fp32", "tile": "256x256, 4 waves, 128-byte K slices",
+                   "accumulate": "fp32",
+                   "tile": (f"{tile[0]}x{tile[1]}" if tile else "auto") + ", 4 waves, 128-byte K slices",
                    "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
     L.tgemm_init.restype = ctypes.c_int
     L.tgemm_last_error.argtypes = []
     L.tgemm_last_error.restype = ctypes.c_char_p
+    L.tgemm_set_tile.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.tgemm_set_tile.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -63,6 +65,12 @@ def check(rc: int) -> None:
 
 def init() -> None:
     check(lib().tgemm_init())
+
+
+def set_tile(tile_m: int = 0, tile_n: int = 0) -> None:
+    """Force the output tile of this thread's later calls; (0, 0) restores
+    the library's own choice (tgemm_set_tile)."""
+    check(lib().tgemm_set_tile(tile_m, tile_n))
 
 
 def _torch():

@@ -18,6 +18,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-command-line-argument", "-fvisibility=hidden",
+    # (Device helpers are unused in the host pass, which compiles no kernel bodies.)
+    "-Wno-unneeded-internal-declaration",
     # No packed-fp32 VALU instructions (v_pk_*_f32) in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

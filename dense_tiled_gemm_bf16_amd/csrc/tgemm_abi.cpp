@@ -33,7 +33,11 @@ int fail(int code, const char *fmt, ...) {
 constexpr int kMaxDevices = 64;
 std::once_flag g_once[kMaxDevices];
 int g_dev_status[kMaxDevices];  // 0 ok, else TGEMM_EHIP
+int g_dev_cus[kMaxDevices];     // compute units
 char g_dev_msg[kMaxDevices][256];
+
+// Tile override of this host thread (tgemm_set_tile); 0, 0 = automatic.
+thread_local int g_tile_m = 0, g_tile_n = 0;
 
 void init_device(int dev) {
   hipDeviceProp_t prop;
@@ -49,17 +53,19 @@ void init_device(int dev) {
              dev, prop.gcnArchName);
     return;
   }
+  g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   g_dev_status[dev] = TGEMM_OK;
 }
 
 // Current device, set up once.  Returns TGEMM_OK or TGEMM_EHIP (message set).
-int ensure_device() {
+int ensure_device(int *cus = nullptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(TGEMM_EHIP, "no usable HIP device: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices) return fail(TGEMM_EHIP, "device index %d out of range", dev);
   std::call_once(g_once[dev], init_device, dev);
   if (g_dev_status[dev] != TGEMM_OK) return fail(g_dev_status[dev], "%s", g_dev_msg[dev]);
+  if (cus) *cus = g_dev_cus[dev];
   return TGEMM_OK;
 }
 
@@ -105,9 +111,14 @@ int check_common(const char *fn, int64_t M, int64_t N, int64_t K, int k_multiple
   return TGEMM_OK;
 }
 
-int dispatch(const char *fn, const tgemm::Problem &p) {
-  int rc = ensure_device();
+int dispatch(const char *fn, tgemm::Problem p) {
+  int rc = ensure_device(&p.cus);
   if (rc != TGEMM_OK) return rc;
+  p.tile_m = g_tile_m;
+  p.tile_n = g_tile_n;
+  if (p.tile_m != 0 && !tgemm::shape_supported(p.kind, p.tile_m, p.tile_n))
+    return fail(TGEMM_EINVAL, "%s: no %dx%d tile for this entry point (set by tgemm_set_tile)", fn, p.tile_m,
+                p.tile_n);
   hipError_t e = tgemm::launch(p);
   if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   return TGEMM_OK;
@@ -124,6 +135,16 @@ int tgemm_init(void) {
 
 const char *tgemm_last_error(void) { return g_err; }
 
+int tgemm_set_tile(int tile_m, int tile_n) {
+  g_err[0] = '\0';
+  const bool known = (tile_m == 0 && tile_n == 0) || (tile_m == 256 && tile_n == 256) ||
+                     (tile_m == 256 && tile_n == 192) || (tile_m == 128 && tile_n == 128);
+  if (!known) return fail(TGEMM_EINVAL, "tgemm_set_tile: no %dx%d tile (256x256, 256x192, 128x128 or 0x0)", tile_m, tile_n);
+  g_tile_m = tile_m;
+  g_tile_n = tile_n;
+  return TGEMM_OK;
+}
+
 int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C, hipStream_t stream) {
   static const char fn[] = "gemm_bf16_nt";
   g_err[0] = '\0';
@@ -133,7 +154,7 @@ int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B, 
   if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
   if ((uint64_t)tgemm::kTileM * k * 2 > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
-  tgemm::Problem p{tgemm::Kind::kBf16NT, M, N, K, A, B, nullptr, nullptr, C, stream};
+  tgemm::Problem p{tgemm::Kind::kBf16NT, M, N, K, A, B, nullptr, nullptr, C, stream, 0, 0, 0};
   return dispatch(fn, p);
 }
 
@@ -148,7 +169,7 @@ int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, v
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
   if (k * n * 2 > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: B too large (K * N * 2 bytes must stay below 2^31)", fn);
-  tgemm::Problem p{tgemm::Kind::kF16NN, M, N, K, A, B, nullptr, nullptr, C, stream};
+  tgemm::Problem p{tgemm::Kind::kF16NN, M, N, K, A, B, nullptr, nullptr, C, stream, 0, 0, 0};
   return dispatch(fn, p);
 }
 
@@ -168,7 +189,7 @@ int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K bytes must stay below 2^31)", fn, (long long)K);
   if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
-  tgemm::Problem p{tgemm::Kind::kMxfp8NT, M, N, K, A, B, scale_A, scale_B, C, stream};
+  tgemm::Problem p{tgemm::Kind::kMxfp8NT, M, N, K, A, B, scale_A, scale_B, C, stream, 0, 0, 0};
   return dispatch(fn, p);
 }
 

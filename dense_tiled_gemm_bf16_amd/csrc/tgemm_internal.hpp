@@ -18,13 +18,19 @@ struct Problem {
   const void *scale_A, *scale_B;  // mxfp8 only
   void *C;
   hipStream_t stream;
+  int cus;             // compute units of the device
+  int tile_m, tile_n;  // forced output tile, or 0, 0 to choose by shape
 };
 
-// Output tile of one workgroup (rows of C x columns of C).
+// Largest output tile of one workgroup (rows of C x columns of C).
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 
-// Enqueues the kernel for `p` on p.stream.  Returns the launch status.
+// Enqueues the kernel for `p` on p.stream.  Returns the launch status
+// (hipErrorInvalidValue for a forced tile the kind does not have).
 hipError_t launch(const Problem &p);
+
+// Whether `kind` has a kernel for output tiles of tile_m x tile_n.
+bool shape_supported(Kind kind, int tile_m, int tile_n);
 
 }  // namespace tgemm

@@ -1,10 +1,11 @@
 // Tiled dense GEMM kernels for gfx950 (MI355X, CDNA4).
 //
 // One workgroup of 256 threads (4 wave64s in a 2 x 2 grid) computes a
-// 256 x 256 tile of C; each wave owns a 128 x 128 sub-tile of fp32
-// accumulators (256 per lane, in AGPRs).  The K loop walks 128-byte slices
-// of the A and B panels (64 bf16/fp16 or 128 fp8 elements per row) through
-// two LDS slots of 32 KiB per operand.
+// TM x TN tile of C -- 256 x 256, or 256 x 192 and 128 x 128 where that
+// fills the chip better -- and each wave a TM/2 x TN/2 sub-tile of fp32
+// accumulators (in AGPRs; 256 per lane for 256 x 256).  The K loop walks
+// 128-byte slices of the A and B panels (64 bf16/fp16 or 128 fp8 elements
+// per row) through two LDS slots per operand.
 //
 // Where this follows the pages and where it departs:
 //  * tile grid: ceil-div over N and M as in the TileLang SM100 README
@@ -67,10 +68,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
 constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;                  // bytes of one tile row per K slice
-constexpr int kSlotBytes = kTileM * kRowBytes;  // one operand, one slot: 32 KiB
 constexpr uint32_t kOOB = 0x80000000u;          // voffset that is always out of range
-
-static_assert(kTileM == 256 && kTileN == 256, "kernel assumes 256 x 256 tiles");
 
 struct Args {
   const uint8_t *A;
@@ -164,17 +162,20 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tiles_m, int tiles_
 
 // ---------------------------------------------------------------------------
 // Staging of one K slice of a K-contiguous panel (A of every kind, B of the
-// NT kinds) into a slot of 256 rows x 128 bytes.  Wave w moves rows
-// [64 w, 64 w + 64) with 8 direct-to-LDS instructions of 8 rows each; lane
-// l of instruction i writes LDS bytes [16 l, 16 l + 16) of its 1 KiB row
-// group, i.e. row 64 w + 8 i + l / 8, physical chunk l % 8, and therefore
-// fetches logical chunk (l % 8) ^ swz(row) of that row.  swz(row) =
-// (4 i + l / 16) & 7 depends on i only through its parity.
+// NT kinds) of 32 NI rows into a slot of 32 NI rows x 128 bytes.  Wave w
+// moves rows [8 NI w, 8 NI (w + 1)) with NI direct-to-LDS instructions of 8
+// rows each; lane l of instruction i writes LDS bytes [16 l, 16 l + 16) of
+// its 1 KiB row group, i.e. row 8 NI w + 8 i + l / 8, physical chunk l % 8,
+// and therefore fetches logical chunk (l % 8) ^ swz(row) of that row.
+// swz(row) = (4 NI w + 4 i + l / 16) & 7 = (4 i + l / 16) & 7 for even NI:
+// it depends on i only through its parity.
 // ---------------------------------------------------------------------------
+template <int NI>
 struct PanelLoader {
+  static_assert(NI % 2 == 0, "the swizzle phase of a wave's first row must not depend on the wave");
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[8];  // per instruction: byte offset of this lane's chunk at slice 0
-  int kcol[2];      // element column of this lane's chunk inside a slice (even / odd i)
+  uint32_t off[NI];  // per instruction: byte offset of this lane's chunk at slice 0
+  int kcol[2];       // element column of this lane's chunk inside a slice (even / odd i)
 
   __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int elem, int wave,
                                        int lane) {
@@ -182,8 +183,8 @@ struct PanelLoader {
 #pragma unroll
     for (int p = 0; p < 2; ++p) kcol[p] = ((lane & 7) ^ swz(8 * p + (lane >> 3))) * (16 / elem);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave * 64 + i * 8 + (lane >> 3);
+    for (int i = 0; i < NI; ++i) {
+      const int r = wave * 8 * NI + i * 8 + (lane >> 3);
       off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem : kOOB;
     }
   }
@@ -192,40 +193,45 @@ struct PanelLoader {
   // slice, or a slice past the end) takes an out-of-range offset.
   __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k, int i) const {
     const bool ok = kt * slice_k + kcol[i & 1] < K;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + wave * 8192 + i * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
                                              ok ? off[i] : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
   }
 };
 
 // ---------------------------------------------------------------------------
-// Staging of one K slice of the NN B operand (K x N, N-contiguous) into a
-// slot of 64 K rows x 512 bytes.  Wave w moves K rows [16 w, 16 w + 16) with
-// 8 instructions of 2 rows each; lane l of instruction i writes row
-// 16 w + 2 i + l / 32, physical chunk l % 32, fetching logical chunk
-// (l % 32) ^ swz_nn(row), i.e. columns n0 + 8 chunk .. + 8.
+// Staging of one K slice of the NN B operand (K x N, N-contiguous) for a
+// tile of TN columns into a slot of 64 K rows x 2 TN bytes.  Wave w moves K
+// rows [16 w, 16 w + 16) with NI = TN / 32 instructions of RPI = 512 / TN
+// rows each; lane l of instruction i writes row 16 w + RPI i + l / LPR
+// (LPR = TN / 8 lanes per row), physical chunk l % LPR, fetching logical
+// chunk (l % LPR) ^ swz_nn(row), i.e. columns n0 + 8 chunk .. + 8.
 // ---------------------------------------------------------------------------
+template <int TN>
 struct NNLoader {
+  // (Instantiated, unused, for the NT kinds' other widths; the NN kernels
+  // use TN = 256 or 128, where an instruction covers whole rows.)
+  static constexpr int NI = TN / 32, RPI = 512 / TN, LPR = TN / 8;
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[8];  // per instruction: byte offset at slice 0 (kOOB past N)
-  int krow0;        // K row of instruction 0 inside the slice
+  uint32_t off[NI];  // per instruction: byte offset at slice 0 (kOOB past N)
+  int krow0;         // K row of instruction 0 inside the slice
   uint32_t slice_bytes;
 
   __device__ __forceinline__ void init(const uint8_t *B, int K, int N, int n0, int wave, int lane) {
     rsrc = make_rsrc(B, (uint32_t)K * (uint32_t)N * 2u);
     const uint32_t row_bytes = (uint32_t)N * 2u;
     slice_bytes = 64u * row_bytes;
-    krow0 = wave * 16 + (lane >> 5);
+    krow0 = wave * 16 + lane / LPR;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kr = krow0 + 2 * i;
-      const int n = n0 + ((lane & 31) ^ swz_nn(kr)) * 8;
+    for (int i = 0; i < NI; ++i) {
+      const int kr = krow0 + RPI * i;
+      const int n = n0 + ((lane % LPR) ^ swz_nn(kr)) * 8;
       off[i] = n < N ? (uint32_t)kr * row_bytes + (uint32_t)n * 2u : kOOB;
     }
   }
 
   __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int i) const {
-    const bool ok = kt * 64 + krow0 + 2 * i < K;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + wave * 8192 + i * 1024), 16,
+    const bool ok = kt * 64 + krow0 + RPI * i < K;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
                                              ok ? off[i] : kOOB, (uint32_t)kt * slice_bytes, 0, 0);
   }
 };
@@ -239,10 +245,13 @@ struct Slots {
   LDS_AS uint8_t *junk;  // 256 bytes per wave: landing area of the L2 prefetches
 };
 
-template <int KIND>
+template <int KIND, int TM, int TN>
 struct Kernel {
   using T = Traits<KIND>;
   static constexpr int kElem = T::kElem;
+  static constexpr int kWM = TM / 2, kWN = TN / 2;   // wave tile (2 x 2 waves)
+  static constexpr int kSlotA = TM * kRowBytes;      // one slot of A, of B (NN: 64 K rows x 2 TN bytes)
+  static constexpr int kSlotB = TN * kRowBytes;
   static constexpr int kSliceK = kRowBytes / kElem;  // K elements per slice
   // MFMA shape.  16-bit inputs: v_mfma_f32_16x16x32 (it reads and writes 4
   // accumulators per 16 K flops, half the accumulator traffic per flop of
@@ -251,10 +260,16 @@ struct Kernel {
   // form.  Either way a slice is two K substeps.
   static constexpr bool kW = T::kScaled;        // 32 x 32 blocks
   static constexpr int kBlk = kW ? 32 : 16;
-  static constexpr int kNB = 128 / kBlk;        // blocks per wave along M and along N
-  static constexpr int kPerSub = kNB * kNB;     // MFMAs per substep
+  static constexpr int kNBm = kWM / kBlk;       // blocks per wave along M (y blocks)
+  static constexpr int kNBn = kWN / kBlk;       // blocks per wave along N (x blocks)
+  static constexpr int kNR = kNBm + kNBn;       // fragment reads per substep
+  static constexpr int kPerSub = kNBm * kNBn;   // MFMAs per substep
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
-  static constexpr int kLoads = 16;             // load instructions per thread per slice (8 A, 8 B)
+  static constexpr int kLA = TM / 32, kLB = TN / 32;  // load instructions per wave per slice
+  static constexpr int kLoads = kLA + kLB;
+  static_assert(!T::kScaled || (TM == 256 && TN == 256), "the block-scaled kernel uses 256 x 256 tiles");
+  static_assert(!T::kNN || TN == 256 || TN == 128, "NN tiles are 256 or 128 columns wide");
+  static_assert(kWM % kBlk == 0 && kWN % kBlk == 0, "wave tile");
   // Schedule, in MFMAs of a slice: the wait + barrier go before MFMA
   // kBarrierAt; the 16 loads of slice kt + 2 go out evenly over the kWindow
   // MFMAs from there on (running into slice kt + 1), which leaves
@@ -265,7 +280,8 @@ struct Kernel {
   // for the 128-MFMA 16-bit slice, three quarters for the 32-MFMA fp8 slice.
   static constexpr int kBarrierAt = T::kScaled ? kMfma * 3 / 4 : kMfma / 2;
   static constexpr int kWindow = kMfma / 2;
-  static_assert(kBarrierAt + 2 * kNB <= kMfma, "next-slice fragment reads must fit after the barrier");
+  static_assert(kBarrierAt + kNR <= kMfma, "next-slice fragment reads must fit after the barrier");
+  static_assert(kNR <= kBarrierAt, "this slice's second-substep reads come before the barrier");
   static_assert(kWindow <= kMfma && kWindow >= kLoads, "load window");
 
   // L2 prefetch (fp8 only).  A slice's lines are first touched by its loads
@@ -309,7 +325,7 @@ struct Kernel {
   using Frag = typename std::conditional<kW, i32x8, u32x4>::type;
   using Acc = typename std::conditional<kW, f32x16, f32x4>::type;
   struct Frags {
-    Frag x[kNB], y[kNB];
+    Frag x[kNBn], y[kNBm];
   };
 
   const Args &a;
@@ -317,8 +333,9 @@ struct Kernel {
   int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
-  PanelLoader la, lb;
-  NNLoader lnn;
+  PanelLoader<kLA> la;
+  PanelLoader<kLB> lb;
+  NNLoader<TN> lnn;
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
   // Block scales (fp8).  They are fetched once per group of 4 slices: a
@@ -333,7 +350,7 @@ struct Kernel {
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside that dword pair
   uint32_t sc_raw[4][2];          // the next group, in flight
   int sc_nxt[8], sc_cur[8];       // per block (4 x blocks, then 4 y blocks): bytes of 4 slices
-  Acc acc[kNB][kNB];
+  Acc acc[kNBn][kNBm];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
 
@@ -372,7 +389,7 @@ struct Kernel {
       const int kr = 32 * sub + 8 * g + 4 * t + e;
       // (Masked to the slot so the compiler can see the read stays inside it
       // and needs no wait for loads into the other slot.)
-      const int off = (kr * 512 + (((n >> 3) ^ swz_nn(kr)) << 4) + (n & 7) * 2) & (kSlotBytes - 1);
+      const int off = (kr * (2 * TN) + (((n >> 3) ^ swz_nn(kr)) << 4) + (n & 7) * 2) & (kSlotB - 1);
       const LDS_AS uint8_t *p = slot + off;
       s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)p);
       u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -419,22 +436,22 @@ struct Kernel {
   __device__ __forceinline__ void fence_acc() {
     mfma_fence();
 #pragma unroll
-    for (int i = 0; i < kNB; ++i)
+    for (int i = 0; i < kNBn; ++i)
 #pragma unroll
-      for (int j = 0; j < kNB; ++j) asm volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < kNBm; ++j) asm volatile("" : "+a"(acc[i][j]));
   }
 
-  // Fragment read R (0 .. 2 kNB - 1) of substep `sub` of slot S: x blocks,
+  // Fragment read R (0 .. kNR - 1) of substep `sub` of slot S: x blocks,
   // then y blocks.
   template <int S, int R>
   __device__ __forceinline__ void read_one(Frags &f, int sub) const {
-    if constexpr (R < kNB) {
+    if constexpr (R < kNBn) {
       if constexpr (T::kNN)
-        f.x[R] = read_cols(slots.b[S], wave_n * 128 + R * kBlk, sub);
+        f.x[R] = read_cols(slots.b[S], wave_n * kWN + R * kBlk, sub);
       else
-        f.x[R] = read_rows(slots.b[S], wave_n * 128 + R * kBlk, sub);
+        f.x[R] = read_rows(slots.b[S], wave_n * kWN + R * kBlk, sub);
     } else {
-      f.y[R - kNB] = read_rows(slots.a[S], wave_m * 128 + (R - kNB) * kBlk, sub);
+      f.y[R - kNBn] = read_rows(slots.a[S], wave_m * kWM + (R - kNBn) * kBlk, sub);
     }
   }
 
@@ -443,15 +460,16 @@ struct Kernel {
     (read_one<S, R>(f, sub), ...);
   }
 
-  // Load instruction i (0..15) of slice kt into slot S: A panel, then B.
+  // Load instruction i (0 .. kLoads - 1) of slice kt into slot S: A panel,
+  // then B.
   template <int S>
   __device__ __forceinline__ void load_one(int kt, int i) {
-    if (i < 8) {
+    if (i < kLA) {
       la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
     } else if constexpr (T::kNN) {
-      lnn.issue(slots.b[S], wave, kt, a.K, i - 8);
+      lnn.issue(slots.b[S], wave, kt, a.K, i - kLA);
     } else {
-      lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - 8);
+      lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
     }
   }
 
@@ -487,8 +505,8 @@ struct Kernel {
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
-  // inside it x block q / kNB times y block q % kNB.  Interleaved with it:
-  //  * Q < 2 kNB: read Q of substep 1 of this slot into f1;
+  // inside it x block q / kNBm times y block q % kNBm.  Interleaved with it:
+  //  * Q < kNR: read Q of substep 1 of this slot into f1;
   //  * before Q = kBarrierAt: wait for this wave's loads of slice kt + 1 and
   //    synchronise the workgroup (slot kt % 2 is then free);
   //  * from kBarrierAt: reads of substep 0 of slice kt + 1 into f0;
@@ -497,7 +515,7 @@ struct Kernel {
   template <int S, int JB, bool FIRST, int Q>
   __device__ __forceinline__ void mfma_one(int kt, Frags &f0, Frags &f1) {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
-    constexpr int I = q / kNB, J = q % kNB;
+    constexpr int I = q / kNBm, J = q % kNBm;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
     if constexpr (Q == kBarrierAt) {
       // The prefetch issued after the last needed load may be outstanding
@@ -508,8 +526,8 @@ struct Kernel {
       // Scales of the next group: waited for by the next slice's barrier.
       if constexpr (T::kScaled && JB == 1) load_scale_group((kt + 3) >> 2);
     }
-    if constexpr (Q < 2 * kNB) read_one<S, Q>(f1, 1);
-    if constexpr (Q >= kBarrierAt && Q - kBarrierAt < 2 * kNB) read_one<S ^ 1, Q - kBarrierAt>(f0, 0);
+    if constexpr (Q < kNR) read_one<S, Q>(f1, 1);
+    if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNR) read_one<S ^ 1, Q - kBarrierAt>(f0, 0);
     if constexpr (kHead >= 0) load_one<S ^ 1>(kt + 1, kHead);
     if constexpr (kTail >= 0) load_one<S>(kt + 2, kTail);
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
@@ -548,23 +566,23 @@ struct Kernel {
 
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
-    m0 = tm * kTileM;
-    n0 = tn * kTileN;
+    m0 = tm * TM;
+    n0 = tn * TN;
     const int K = a.K;
     nk = a.ksteps;
 
-    la.init(a.A + (size_t)m0 * K * kElem, min(a.M - m0, kTileM), K, kElem, wave, lane);
+    la.init(a.A + (size_t)m0 * K * kElem, min(a.M - m0, TM), K, kElem, wave, lane);
     if constexpr (T::kNN)
       lnn.init(a.B, K, a.N, n0, wave, lane);
     else
-      lb.init(a.B + (size_t)n0 * K * kElem, min(a.N - n0, kTileN), K, kElem, wave, lane);
+      lb.init(a.B + (size_t)n0 * K * kElem, min(a.N - n0, TN), K, kElem, wave, lane);
     if constexpr (kPfDist > 0) {
       // Waves 0-1 take 32 rows of the A panel (its share among the 8 tile
       // columns of an XCD's block), waves 2-3 take 64 rows of the B panel
       // (its share among the 4 tile rows).
       const bool is_a = wave < 2;
       pf_rsrc = is_a ? la.rsrc : lb.rsrc;
-      const int rows_valid = is_a ? min(a.M - m0, kTileM) : min(a.N - n0, kTileN);
+      const int rows_valid = is_a ? min(a.M - m0, TM) : min(a.N - n0, TN);
       const int r = is_a ? 32 * (tn & 7) + 16 * wave + (lane & 15) : 64 * (tm & 3) + 32 * (wave - 2) + (lane & 31);
       const bool active = is_a ? lane < 16 : lane < 32;
       pf_off = active && r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)kElem : kOOB;
@@ -578,7 +596,7 @@ struct Kernel {
       for (int op = 0; op < 2; ++op) {
         const uintptr_t start = (uintptr_t)(op ? a.SA + (size_t)m0 * a.kb : a.SB + (size_t)n0 * a.kb);
         const uint32_t mis = (uint32_t)(start & 3);
-        const int rows_valid = op ? min(a.M - m0, kTileM) : min(a.N - n0, kTileN);
+        const int rows_valid = op ? min(a.M - m0, TM) : min(a.N - n0, TN);
         rss[op] = make_rsrc((const void *)(start - mis), (mis + (uint32_t)rows_valid * (uint32_t)a.kb + 3) & ~3u);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -590,9 +608,9 @@ struct Kernel {
         }
       }
 #pragma unroll
-      for (int i = 0; i < kNB; ++i)
+      for (int i = 0; i < kNBn; ++i)
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) acc[i][j] = Acc{};
+        for (int j = 0; j < kNBm; ++j) acc[i][j] = Acc{};
     }
 
     // Prologue: the scales of slices 0-3, slice 0 into slot 0, the loads
@@ -612,7 +630,7 @@ struct Kernel {
     }
     barrier();
     Frags f0, f1;
-    read_all<0>(std::make_integer_sequence<int, 2 * kNB>(), f0, 0);
+    read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
     // Slice 0 starts the accumulators; then slices go two (fp8: four) at a
     // time, alternating slots.  The count is padded: a slice past nk
     // arrives as zeros and adds nothing.  (Leaving the loop early instead
@@ -638,8 +656,8 @@ struct Kernel {
     epilogue();
   }
 
-  // acc[i][j] covers B rows (C columns) n0 + 128 wave_n + kBlk i and A rows
-  // (C rows) m0 + 128 wave_m + kBlk j.  32 x 32 blocks: lane l, register r
+  // acc[i][j] covers B rows (C columns) n0 + kWN wave_n + kBlk i and A rows
+  // (C rows) m0 + kWM wave_m + kBlk j.  32 x 32 blocks: lane l, register r
   // holds C row l % 32 of the block, column 8 (r / 4) + 4 (l / 32) + r % 4.
   // 16 x 16 blocks: lane l, register r holds row l % 16, column
   // 4 (l / 16) + r.  Either way four consecutive columns leave as one
@@ -649,15 +667,15 @@ struct Kernel {
     const int row_l = lane % kBlk;
     const int colq = kBlk == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) {
-      const int m = m0 + wave_m * 128 + j * kBlk + row_l;
+    for (int j = 0; j < kNBm; ++j) {
+      const int m = m0 + wave_m * kWM + j * kBlk + row_l;
       if (m >= a.M) continue;
       uint8_t *crow = a.C + (size_t)m * a.N * 2;
 #pragma unroll
-      for (int i = 0; i < kNB; ++i) {
+      for (int i = 0; i < kNBn; ++i) {
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-          const int n = n0 + wave_n * 128 + i * kBlk + g * 8 + colq;
+          const int n = n0 + wave_n * kWN + i * kBlk + g * 8 + colq;
           if (n >= a.N) continue;
           const f32x2 lo = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]};
           const f32x2 up = {acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
@@ -676,15 +694,23 @@ struct Kernel {
   }
 };
 
-template <int KIND>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(const Args a) {
+// Workgroups per CU a tile shape is built for: the 256-row shapes fill a
+// SIMD's registers with one wave; 128 x 128 tiles (64 x 64 per wave) leave
+// room for two workgroups per CU, which hide each other's waits.
+template <int TM, int TN>
+constexpr int kWgPerCu = TM * TN <= 128 * 128 ? 2 : 1;
+
+template <int KIND, int TM, int TN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWgPerCu<TM, TN>, kWgPerCu<TM, TN>)))
+void gemm_kernel(const Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body is device code only; the host pass needs the symbol
   // Four separate arrays (not one indexed array) so the compiler can tell
   // the slot being loaded from the slot being read and does not insert a
   // vmcnt wait in front of every LDS read.
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[TM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[TN * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[TN * kRowBytes];
   __shared__ __attribute__((aligned(256))) uint8_t junk[4 * 256];
   Slots slots;
   slots.a[0] = (LDS_AS uint8_t *)sA0;
@@ -692,8 +718,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
   slots.junk = (LDS_AS uint8_t *)junk;
-  Kernel<KIND> k(a, slots);
+  Kernel<KIND, TM, TN> k(a, slots);
   k.run();
+#endif
+}
+
+template <int KIND, int TM, int TN>
+hipError_t launch_shape(const Problem &p, Args a) {
+  a.tiles_m = (int)((p.M + TM - 1) / TM);
+  a.tiles_n = (int)((p.N + TN - 1) / TN);
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  hipLaunchKernelGGL((gemm_kernel<KIND, TM, TN>), grid, block, 0, p.stream, a);
+  return hipGetLastError();
+}
+
+// Tile shapes per kind, largest first, each with a rate relative to
+// 256 x 256 per unit of tile area in a wave of workgroups.  The rates are
+// fitted to sustained measurements on MI355X: 128 x 128 tiles run 4096 x
+// 4096 x 8192 at 0.83 of the 256 x 256 speed but fill the chip for small
+// problems (fp16 NN 1024^3: 11.7 us against 30.8 us; bf16 256^3: 5.8 us
+// against 14.7 us), and 256 x 192 turns 4000 x 3000 x 5000 from 192 into
+// 256 tiles (114 us against 117 us: under the power cap the idle CUs of
+// the smaller grid leave clock headroom, so filling them gains little).
+struct Shape {
+  int tm, tn;
+  double rel;
+};
+constexpr Shape kShapesNT[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.45}};
+constexpr Shape kShapesNN[] = {{256, 256, 1.0}, {128, 128, 0.45}};
+
+// The shape with the least estimated time: whole waves of tiles over the
+// CUs, each wave costing its tile area over the shape's relative rate.
+template <size_t NS>
+Shape pick_shape(const Shape (&shapes)[NS], int64_t M, int64_t N, int cus) {
+  Shape best = shapes[0];
+  double best_t = 0;
+  for (size_t i = 0; i < NS; ++i) {
+    const Shape &s = shapes[i];
+    const int64_t tiles = ((M + s.tm - 1) / s.tm) * ((N + s.tn - 1) / s.tn);
+    const int64_t slots = (int64_t)cus * (s.tm * s.tn <= 128 * 128 ? 2 : 1);
+    const int64_t waves = (tiles + slots - 1) / slots;
+    const double t = (double)waves * s.tm * s.tn / s.rel;
+    if (i == 0 || t < best_t) {
+      best = s;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -708,24 +779,44 @@ hipError_t launch(const Problem &p) {
   a.M = (int)p.M;
   a.N = (int)p.N;
   a.K = (int)p.K;
-  a.tiles_m = (int)((p.M + kTileM - 1) / kTileM);
-  a.tiles_n = (int)((p.N + kTileN - 1) / kTileN);
   const int slice = p.kind == Kind::kMxfp8NT ? 128 : 64;
   a.ksteps = (int)((p.K + slice - 1) / slice);
   a.kb = (int)((p.K + 127) / 128);
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  int tm = p.tile_m, tn = p.tile_n;
+  if (tm == 0) {
+    const Shape s = p.kind == Kind::kBf16NT  ? pick_shape(kShapesNT, p.M, p.N, p.cus)
+                    : p.kind == Kind::kF16NN ? pick_shape(kShapesNN, p.M, p.N, p.cus)
+                                             : Shape{256, 256, 1.0};
+    tm = s.tm;
+    tn = s.tn;
+  }
   switch (p.kind) {
     case Kind::kBf16NT:
-      hipLaunchKernelGGL(gemm_kernel<0>, grid, block, 0, p.stream, a);
+      if (tm == 256 && tn == 256) return launch_shape<0, 256, 256>(p, a);
+      if (tm == 256 && tn == 192) return launch_shape<0, 256, 192>(p, a);
+      if (tm == 128 && tn == 128) return launch_shape<0, 128, 128>(p, a);
       break;
     case Kind::kF16NN:
-      hipLaunchKernelGGL(gemm_kernel<1>, grid, block, 0, p.stream, a);
+      if (tm == 256 && tn == 256) return launch_shape<1, 256, 256>(p, a);
+      if (tm == 128 && tn == 128) return launch_shape<1, 128, 128>(p, a);
       break;
     case Kind::kMxfp8NT:
-      hipLaunchKernelGGL(gemm_kernel<2>, grid, block, 0, p.stream, a);
+      if (tm == 256 && tn == 256) return launch_shape<2, 256, 256>(p, a);
       break;
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
+}
+
+bool shape_supported(Kind kind, int tile_m, int tile_n) {
+  switch (kind) {
+    case Kind::kBf16NT:
+      return (tile_m == 256 && (tile_n == 256 || tile_n == 192)) || (tile_m == 128 && tile_n == 128);
+    case Kind::kF16NN:
+      return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128);
+    case Kind::kMxfp8NT:
+      return tile_m == 256 && tile_n == 256;
+  }
+  return false;
 }
 
 }  // namespace tgemm

@@ -129,6 +129,23 @@ TGEMM_API int tgemm_init(void);
  */
 TGEMM_API const char *tgemm_last_error(void);
 
+/*
+ * Output tile override for the calling host thread's later calls, for
+ * tuning and tests.  Each workgroup computes a tile_m x tile_n block of C;
+ * by default (0, 0) the library picks, per call, the shape that needs the
+ * fewest waves of workgroups for the least work (the pages' kernels take
+ * their block sizes as parameters: SM100 README, "Code Example",
+ * block_M / block_N; velog "tilelang", 1.1 Front-End DSL).
+ *   gemm_bf16_nt:  256x256, 256x192, 128x128
+ *   gemm_f16_nn:   256x256, 128x128
+ *   gemm_mxfp8_nt: 256x256
+ * Returns TGEMM_OK, or TGEMM_EINVAL for a shape no entry point has; an
+ * entry point called with a shape it does not have returns TGEMM_EINVAL.
+ * The result does not depend on the tile shape beyond the order of the
+ * fp32 summation.
+ */
+TGEMM_API int tgemm_set_tile(int tile_m, int tile_n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,9 +27,9 @@ def declared_functions():
     return re.findall(r"^TGEMM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "tgemm_init", "tgemm_last_error"])
+        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "tgemm_init", "tgemm_last_error", "tgemm_set_tile"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -138,3 +138,13 @@ def test_no_device_is_an_error_not_a_crash():
         pytest.skip("a GPU is present; the no-device path cannot be exercised")
     assert tg.lib().tgemm_init() == tg.EHIP
     assert "HIP device" in tg.last_error() or "hip" in tg.last_error().lower()
+
+
+def test_set_tile_validates_shapes():
+    L = tg.lib()
+    assert L.tgemm_set_tile(100, 100) == tg.EINVAL
+    assert "no 100x100 tile" in tg.last_error()
+    assert L.tgemm_set_tile(256, 128) == tg.EINVAL
+    for tm, tn in [(256, 256), (256, 192), (128, 128), (0, 0)]:
+        assert L.tgemm_set_tile(tm, tn) == tg.OK
+        assert tg.last_error() == ""

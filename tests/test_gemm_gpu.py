@@ -230,6 +230,55 @@ def test_mid_size_full_parity_several_tiles(kind):
     assert_close(kind, to_bits(run(kind, x, M, N, K)), oracle_full(kind, x), f"{kind} {M}x{N}x{K}")
 
 
+# --- every tile shape, forced ----------------------------------------------------------
+
+SHAPES = [("bf16_nt", 256, 256), ("bf16_nt", 256, 192), ("bf16_nt", 128, 128),
+          ("f16_nn", 256, 256), ("f16_nn", 128, 128), ("mxfp8_nt", 256, 256)]
+
+
+@pytest.fixture
+def forced_tile():
+    def force(tm, tn):
+        tg.set_tile(tm, tn)
+    yield force
+    tg.set_tile(0, 0)
+
+
+@pytest.mark.parametrize("kind,tm,tn", SHAPES)
+def test_tile_shape_tails(kind, tm, tn, forced_tile):
+    """Each tile shape over ragged M, N and K: random inputs within the
+    tolerance, integer inputs bitwise."""
+    forced_tile(tm, tn)
+    Ks = [16, 144, 400] if kind == "mxfp8_nt" else [8, 72, 200]
+    for K in Ks:
+        for M in [1, 129, 300]:
+            for N in [8, 200, 264]:
+                x = workloads.make_random(kind, M, N, K, seed=M * 5 + N * 11 + K + tn)
+                assert_close(kind, to_bits(run(kind, x, M, N, K)), oracle_full(kind, x),
+                             f"{kind} {tm}x{tn} {M}x{N}x{K}")
+                xi = workloads.make_integer(kind, M, N, K, seed=M + N * 3 + K + tm)
+                assert_bitwise(to_bits(run(kind, xi, M, N, K)), oracle_full(kind, xi),
+                               f"{kind} {tm}x{tn} int {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kind,tm,tn", SHAPES)
+def test_tile_shape_mid_size_full_parity(kind, tm, tn, forced_tile):
+    forced_tile(tm, tn)
+    M, N, K = 776, 520, 1040 if kind != "mxfp8_nt" else 1024
+    x = workloads.make_random(kind, M, N, K, seed=13)
+    assert_close(kind, to_bits(run(kind, x, M, N, K)), oracle_full(kind, x), f"{kind} {tm}x{tn}")
+
+
+def test_tile_shape_missing_for_entry_point_is_rejected(forced_tile):
+    forced_tile(128, 128)
+    a = torch.zeros(64, 64, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(64, 1, dtype=torch.uint8, device="cuda")
+    c = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    rc = tg.lib().gemm_mxfp8_nt(64, 64, 64, a.data_ptr(), a.data_ptr(), s.data_ptr(), s.data_ptr(),
+                                c.data_ptr(), None)
+    assert rc == tg.EINVAL and "no 128x128 tile" in tg.last_error()
+
+
 @pytest.mark.parametrize("kind", ["bf16_nt", "f16_nn", "mxfp8_nt"])
 def test_K_zero_writes_zeros(kind):
     M, N = 70, 40
