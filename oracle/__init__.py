@@ -65,6 +65,9 @@ def _load():
         getattr(lib, name).argtypes = [i64, u8p, f64p]
     for name in ("oracle_encode_bf16", "oracle_encode_f16"):
         getattr(lib, name).argtypes = [i64, f64p, u16p]
+    lib.oracle_encode_e4m3fn.argtypes = [i64, f64p, u8p]
+    lib.oracle_quantize_mxfp8.argtypes = [i64, i64, ctypes.c_void_p, u8p, u8p]
+    lib.oracle_quantize_mxfp8.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -128,6 +131,27 @@ def encode_f16(x) -> np.ndarray:
     out = np.empty(x.shape, np.uint16)
     _load().oracle_encode_f16(x.size, _ptr(x), _ptr(out))
     return out
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """binary64 -> e4m3fn bytes, round to nearest even (|x| <= 448)."""
+    x = _c(np.asarray(x, np.float64), np.float64)
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_encode_e4m3fn(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+# --- block-scale quantiser -----------------------------------------------------
+
+def quantize_mxfp8(x):
+    """float32 (R, K) -> (q uint8 (R, K) e4m3fn, s uint8 (R, ceil(K/128)) e8m0):
+    per row and 128-K block the smallest 2^e with absmax <= 448 * 2^e."""
+    x = _c(np.asarray(x), np.float32)
+    R, K = x.shape
+    q = np.empty((R, K), np.uint8)
+    s = np.empty((R, (K + 127) // 128), np.uint8)
+    _load().oracle_quantize_mxfp8(R, K, _ptr(x), _ptr(q), _ptr(s))
+    return q, s
 
 
 # --- full GEMMs ---------------------------------------------------------------

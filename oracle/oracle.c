@@ -163,6 +163,27 @@ uint16_t oracle_f64_to_f16(double x)
     return sign | (uint16_t)((ex + 15) << 10) | f;
 }
 
+/*
+ * binary64 -> OCP FP8 E4M3FN (4 significant bits, emin = -6, bias 7, largest
+ * finite 448 = 0x7e; no infinities, 0x7f/0xff are NaN).  For |x| <= 448
+ * only, which is all the quantiser below produces.
+ */
+uint8_t oracle_f64_to_e4m3fn(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0)
+        return sign;
+    double r = round_to_grid(ax, 4, -6);
+    if (r < ldexp(1.0, -6))          /* subnormal: r = m * 2^-9, m in 0..7 */
+        return sign | (uint8_t)(r * 512.0);
+    int e2;
+    double fr = frexp(r, &e2);       /* r = fr * 2^e2, fr in [0.5, 1) */
+    int ex = e2 - 1;                 /* r = (1 + m/8) * 2^ex */
+    uint8_t m = (uint8_t)(fr * 16.0 - 8.0);
+    return sign | (uint8_t)((ex + 7) << 3) | m;
+}
+
 /* Elementwise array forms, for the tests. */
 void oracle_decode_bf16(int64_t n, const uint16_t *in, double *out)
 {
@@ -187,6 +208,63 @@ void oracle_encode_bf16(int64_t n, const double *in, uint16_t *out)
 void oracle_encode_f16(int64_t n, const double *in, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16(in[i]);
+}
+void oracle_encode_e4m3fn(int64_t n, const double *in, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_e4m3fn(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-scale quantiser.                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The step that makes the block-scaled GEMM's operands: binary32 rows x
+ * (R x K, row-major) to e4m3fn bytes q (R x K) with one e8m0 scale byte per
+ * row per 128 K elements, s (R x ceil(K/128)) -- the granularity of the
+ * Blackwell TCGEN05 GEMM tutorial, section "进阶" (Advanced):
+ * sf_a_granularity_k = sf_b_granularity_k = 128.  The pages give no rule
+ * for choosing a scale; the reading taken is the smallest power of two 2^e
+ * with absmax <= 448 * 2^e (448 = largest e4m3fn), e clamped to
+ * [-127, 127], e = -127 for an all-zero block, stored as the byte e + 127;
+ * each element is x * 2^-e (exact) rounded once to e4m3fn, ties to even.
+ * A last block shorter than 128 (K % 128 != 0) takes the maximum over the
+ * elements it has.  Inputs must be finite.
+ */
+void oracle_quantize_mxfp8(int64_t R, int64_t K, const float *x, uint8_t *q, uint8_t *s)
+{
+    const int64_t KB = (K + 127) / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const int64_t k0 = b * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+            double absmax = 0.0;
+            for (int64_t k = k0; k < k1; ++k) {
+                double a = fabs((double)x[r * K + k]);
+                if (a > absmax)
+                    absmax = a;
+            }
+            int e;
+            if (absmax == 0.0) {
+                e = -127;
+            } else {
+                int e2;
+                (void)frexp(absmax, &e2);        /* 2^(e2-1) <= absmax < 2^e2 */
+                /* 448 * 2^(e2-10) < 2^(e2-1) <= absmax: start below the answer
+                   and take the first e that fits. */
+                e = e2 - 10;
+                while (absmax > ldexp(448.0, e))
+                    ++e;
+                if (e < -127)
+                    e = -127;
+                if (e > 127)
+                    e = 127;
+            }
+            s[r * KB + b] = (uint8_t)(e + 127);
+            for (int64_t k = k0; k < k1; ++k)
+                q[r * K + k] = oracle_f64_to_e4m3fn(ldexp((double)x[r * K + k], -e));
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */
