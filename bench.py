@@ -49,22 +49,32 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "mxfp8": 5033.2}  # MI355X dense MFMA, 256 CU x 2.4 GHz
 METRIC = "TFLOPS (2MNK/t) and % of MFMA peak, bf16 NT GEMM 4096x4096x8192, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "dense_tiled_gemm_bf16_amd", "csrc", "tgemm_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bf16_nt_4096x4096x8192.json")
+CSRC = os.path.join(ROOT, "dense_tiled_gemm_bf16_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "tgemm_kernels.hip")        # the GEMM kernels
+QUANT_SRC = os.path.join(CSRC, "tgemm_quant.hip")           # the quantiser
+
+
+def source_of(kind: str) -> str:
+    return QUANT_SRC if kind == "quant_mxfp8" else KERNEL_SRC
+
+
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{name}.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(text: str | None = None) -> str:
-    """SHA-256 prefix of the kernel source's code: comments and blank lines
+def kernel_source_hash(text: str | None = None, src: str = KERNEL_SRC) -> str:
+    """SHA-256 prefix of a kernel source's code: comments and blank lines
     removed, so that a change to comments alone keeps a counter record."""
     import re
     if text is None:
-        text = open(KERNEL_SRC).read()
+        text = open(src).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln.strip())
@@ -74,11 +84,13 @@ def kernel_source_hash(text: str | None = None) -> str:
 def measured_traffic(name: str):
     """HBM bytes per launch from a committed counter run, if it was taken on
     the current kernel source; else None."""
+    import workloads
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(name)))
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != name or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    src = source_of(workloads.WORKLOADS[name].kind)
+    if rec.get("workload") != name or rec.get("kernel_source_sha256_16") != kernel_source_hash(src=src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -212,11 +224,13 @@ def record_traffic(d: str, name: str):
     dispatch), each scaled by known bytes / counted bytes of a plain copy."""
     import workloads
     w = workloads.WORKLOADS[name]
-    f = lambda stem: os.path.join(d, f"{stem}_counter_collection.csv")
-    is_gemm = lambda k: "gemm_kernel" in k
+    quant = w.kind == "quant_mxfp8"
+    stem = "quant" if quant else "gemm"
+    f = lambda s: os.path.join(d, f"{s}_counter_collection.csv")
+    is_kernel = (lambda k: "quantize_mxfp8_kernel" in k) if quant else (lambda k: "gemm_kernel" in k)
     is_copy = lambda k: "copy" in k.lower()
-    g_fetch, nd_f, gnames = _counter_per_dispatch(f("gemm_fetch"), "FETCH_SIZE", is_gemm)
-    g_write, nd_w, _ = _counter_per_dispatch(f("gemm_write"), "WRITE_SIZE", is_gemm)
+    g_fetch, nd_f, gnames = _counter_per_dispatch(f(stem + "_fetch"), "FETCH_SIZE", is_kernel)
+    g_write, nd_w, _ = _counter_per_dispatch(f(stem + "_write"), "WRITE_SIZE", is_kernel)
     c_fetch, _, cnames = _counter_per_dispatch(f("copy_fetch"), "FETCH_SIZE", is_copy)
     c_write, _, _ = _counter_per_dispatch(f("copy_write"), "WRITE_SIZE", is_copy)
     copy_bytes = COPY_BYTES
@@ -224,10 +238,12 @@ def record_traffic(d: str, name: str):
     kw = copy_bytes / (c_write * 1024.0)
     fetch_b = g_fetch * 1024.0 * kf
     write_b = g_write * 1024.0 * kw
-    out_elem = 2
-    in_bytes = w.M * w.K * (1 if w.kind == "mxfp8_nt" else 2) + w.N * w.K * (1 if w.kind == "mxfp8_nt" else 2)
-    alg = in_bytes + w.M * w.N * out_elem
-    rec = {"workload": name, "kernel_source_sha256_16": kernel_source_hash(),
+    if quant:
+        alg = quant_bytes(w)
+    else:
+        in_bytes = w.M * w.K * (1 if w.kind == "mxfp8_nt" else 2) + w.N * w.K * (1 if w.kind == "mxfp8_nt" else 2)
+        alg = in_bytes + w.M * w.N * 2
+    rec = {"workload": name, "kernel_source_sha256_16": kernel_source_hash(src=source_of(w.kind)),
            "kernel": gnames, "dispatches": [nd_f, nd_w],
            "fetch_kib_per_dispatch": round(g_fetch, 1), "write_kib_per_dispatch": round(g_write, 1),
            "copy_kernel": cnames, "copy_bytes": copy_bytes,
@@ -240,6 +256,85 @@ def record_traffic(d: str, name: str):
     out = os.path.join(d, f"traffic_{name}.json")
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec))
+
+
+def quant_bytes(w) -> int:
+    """Algorithmic bytes of one quantiser launch: x read once, q and the
+    scales written once."""
+    return w.M * w.K * 4 + w.M * w.K + w.M * ((w.K + 127) // 128)
+
+
+def bench_quantize(args, w):
+    """The block-scale quantiser: HBM-bound, reported in GB/s against the
+    8 TB/s HBM peak."""
+    import numpy as np
+    import torch
+    import dense_tiled_gemm_bf16_amd as tg
+    import oracle
+    torch.cuda.set_device(0)
+    tg.init()
+    import workloads
+    x = workloads.make_inputs(w)["X"]
+    xd = torch.from_numpy(x).cuda()
+    KB = (w.K + 127) // 128
+    q = torch.empty((w.M, w.K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((w.M, KB), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    L = tg.lib()
+    argv = (w.M, w.K, xd.data_ptr(), q.data_ptr(), s.data_ptr(), stream.cuda_stream)
+
+    def launch():
+        rc = L.quantize_mxfp8(*argv)
+        if rc != 0:
+            raise RuntimeError(f"quantize_mxfp8: [{rc}] {tg.last_error()}")
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            launch()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for _ in range(args.steps):
+            launch()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    nbytes = quant_bytes(w)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"[bench] {w.description}: {ms*1e3:.2f} us/launch, {gbs:.0f} GB/s of {PEAK_HBM_GBS}")
+    parity = None
+    if not args.no_parity:
+        rows = np.arange(0, w.M, max(1, w.M // 64))
+        qr, sr = oracle.quantize_mxfp8(x[rows])
+        parity = {"rows_checked": int(rows.size),
+                  "elements_differing": int((q.cpu().numpy()[rows] != qr).sum()),
+                  "scales_differing": int((s.cpu().numpy()[rows] != sr).sum())}
+        log(f"[bench] parity sample: {parity}")
+    cpu = None
+    if args.cpu_seconds > 0:
+        # Whole passes over the workload until about cpu_seconds of work.
+        threads = oracle.num_threads()
+        passes, t = 0, time.perf_counter()
+        while passes == 0 or time.perf_counter() - t < args.cpu_seconds:
+            oracle.quantize_mxfp8(x)
+            passes += 1
+        dt = time.perf_counter() - t
+        cpu = {"value": round(nbytes * passes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{passes} whole passes of {w.name} through the oracle quantiser, {dt:.1f} s"}
+    line = {
+        "metric": f"GB/s (algorithmic bytes / t), {w.description}, 1 GPU",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32->fp8e4m3+e8m0", "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "K": w.K},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
+                     "kernel_mean_us": round(ms * 1e3, 2), "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu, "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -275,6 +370,9 @@ def main():
         return
 
     w = workloads.WORKLOADS[args.workload]
+    if w.kind == "quant_mxfp8":
+        bench_quantize(args, w)
+        return
     prec = {"bf16_nt": "bf16", "f16_nn": "f16", "mxfp8_nt": "mxfp8"}[w.kind]
     torch.cuda.set_device(0)
     tg.init()

@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.tgemm_last_error.restype = ctypes.c_char_p
     L.tgemm_set_tile.argtypes = [ctypes.c_int, ctypes.c_int]
     L.tgemm_set_tile.restype = ctypes.c_int
+    L.quantize_mxfp8.argtypes = [i64, i64, p, p, p, p]
+    L.quantize_mxfp8.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -153,3 +155,16 @@ def gemm_mxfp8_nt(a, b, scale_a, scale_b, out=None, stream=None):
     check(lib().gemm_mxfp8_nt(M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
                               scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
     return c
+
+
+def quantize_mxfp8(x, q=None, scales=None, stream=None):
+    """float32 (M,K) -> (q uint8 (M,K) e4m3fn bytes, scales uint8 (M,ceil(K/128))
+    e8m0 bytes), the operands of gemm_mxfp8_nt (quantize_mxfp8 in the C ABI)."""
+    torch = _torch()
+    M, K = x.shape
+    KB = (K + 127) // 128
+    _want(x, "x", torch.float32, (M, K))
+    q = _out(q, (M, K), torch.uint8, x)
+    scales = _out(scales, (M, KB), torch.uint8, x)
+    check(lib().quantize_mxfp8(M, K, x.data_ptr(), q.data_ptr(), scales.data_ptr(), _stream_ptr(stream)))
+    return q, scales

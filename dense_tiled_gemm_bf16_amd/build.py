@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtgemm.so")
-SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_quant.hip"),
+           os.path.join(CSRC, "tgemm_abi.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

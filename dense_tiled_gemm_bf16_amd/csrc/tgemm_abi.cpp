@@ -135,6 +135,32 @@ int tgemm_init(void) {
 
 const char *tgemm_last_error(void) { return g_err; }
 
+int quantize_mxfp8(int64_t M, int64_t K, const float *x, void *q, void *scales, hipStream_t stream) {
+  static const char fn[] = "quantize_mxfp8";
+  g_err[0] = '\0';
+  if (M < 0 || K < 0)
+    return fail(TGEMM_EINVAL, "%s: negative size (M=%lld, K=%lld)", fn, (long long)M, (long long)K);
+  if (M > INT32_MAX || K > INT32_MAX)
+    return fail(TGEMM_ETOOBIG, "%s: sizes must be below 2^31 (M=%lld, K=%lld)", fn, (long long)M, (long long)K);
+  if (M == 0 || K == 0) return TGEMM_OK;
+  if (K % 16 != 0) return fail(TGEMM_EALIGN, "%s: K=%lld must be a multiple of 16", fn, (long long)K);
+  const uint64_t n = (uint64_t)M * (uint64_t)K, kb = ((uint64_t)K + 127) / 128;
+  if (!x) return fail(TGEMM_EINVAL, "%s: x is NULL", fn);
+  if (!q) return fail(TGEMM_EINVAL, "%s: q is NULL", fn);
+  if (!scales) return fail(TGEMM_EINVAL, "%s: scales is NULL", fn);
+  if (misaligned(x)) return fail(TGEMM_EALIGN, "%s: x is not 16-byte aligned", fn);
+  if (misaligned(q)) return fail(TGEMM_EALIGN, "%s: q is not 16-byte aligned", fn);
+  if (overlaps(q, n, x, n * 4)) return fail(TGEMM_EINVAL, "%s: q overlaps x", fn);
+  if (overlaps(scales, (uint64_t)M * kb, x, n * 4)) return fail(TGEMM_EINVAL, "%s: scales overlaps x", fn);
+  if (overlaps(scales, (uint64_t)M * kb, q, n)) return fail(TGEMM_EINVAL, "%s: scales overlaps q", fn);
+  int rc = ensure_device();
+  if (rc != TGEMM_OK) return rc;
+  tgemm::QuantProblem p{M, K, x, q, scales, stream};
+  hipError_t e = tgemm::launch_quantize(p);
+  if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return TGEMM_OK;
+}
+
 int tgemm_set_tile(int tile_m, int tile_n) {
   g_err[0] = '\0';
   const bool known = (tile_m == 0 && tile_n == 0) || (tile_m == 256 && tile_n == 256) ||

@@ -33,4 +33,17 @@ hipError_t launch(const Problem &p);
 // Whether `kind` has a kernel for output tiles of tile_m x tile_n.
 bool shape_supported(Kind kind, int tile_m, int tile_n);
 
+// A validated block-scale quantisation: M, K > 0, K % 16 == 0, x and q
+// 16-byte aligned.
+struct QuantProblem {
+  int64_t M, K;
+  const void *x;  // M x K binary32
+  void *q;        // M x K e4m3fn bytes
+  void *scales;   // M x ceil(K/128) e8m0 bytes
+  hipStream_t stream;
+};
+
+// Enqueues the quantiser for `p` on p.stream.  Returns the launch status.
+hipError_t launch_quantize(const QuantProblem &p);
+
 }  // namespace tgemm

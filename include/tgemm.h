@@ -116,6 +116,30 @@ TGEMM_API int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K,
                   void *C, hipStream_t stream);
 
 /*
+ * Block-scale quantiser: binary32 rows to the operand format of
+ * gemm_mxfp8_nt (the step before the block-scaled GEMM; one scale per 128 K
+ * elements as in the Blackwell TCGEN05 GEMM tutorial, section "进阶"
+ * (Advanced)).
+ *
+ *   x       device pointer, M x K binary32, row-major (finite values)
+ *   q       device pointer, M x K e4m3fn bytes, row-major; written
+ *   scales  device pointer, M x ceil(K/128) e8m0 bytes, row-major; written
+ *
+ * For each row and each block of 128 K elements (the last may be shorter),
+ * the scale is the smallest power of two 2^e with max |x| <= 448 * 2^e
+ * (448 = largest e4m3fn), e clamped to [-127, 127] and e = -127 for an
+ * all-zero block, stored as the byte e + 127; each element is x * 2^-e
+ * rounded to the nearest e4m3fn value, ties to even.  The pages fix the
+ * granularity and format but no rule for the scale: this rule is the
+ * library's.
+ * Requirements: K % 16 == 0; x and q 16-byte aligned (scales need no
+ * alignment); no overlap between the three arrays.  M == 0 or K == 0
+ * writes nothing.
+ */
+TGEMM_API int quantize_mxfp8(int64_t M, int64_t K, const float *x, void *q, void *scales,
+                             hipStream_t stream);
+
+/*
  * Optional, idempotent set-up for the current device: checks that it is a
  * gfx950 GPU.  Returns TGEMM_OK or TGEMM_EHIP.  Entry points call it
  * themselves on first use of a device (the host wrapper's init() on the

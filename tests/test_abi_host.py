@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "tgemm_init", "tgemm_last_error", "tgemm_set_tile"])
+        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "quantize_mxfp8", "tgemm_init", "tgemm_last_error",
+         "tgemm_set_tile"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -148,3 +149,23 @@ def test_set_tile_validates_shapes():
     for tm, tn in [(256, 256), (256, 192), (128, 128), (0, 0)]:
         assert L.tgemm_set_tile(tm, tn) == tg.OK
         assert tg.last_error() == ""
+
+
+def _q(M, K, X=A16, Q=C16, S=0x30000001):
+    return tg.lib().quantize_mxfp8(M, K, X, Q, S, None)
+
+
+def test_quantize_validation():
+    L = tg.lib()
+    assert _q(0, 64, X=None, Q=None, S=None) == tg.OK and _q(64, 0, X=None, Q=None, S=None) == tg.OK
+    assert _q(-1, 64) == tg.EINVAL and "negative size" in tg.last_error()
+    assert _q(16, 24) == tg.EALIGN and "multiple of 16" in tg.last_error()
+    assert _q(16, 64, X=None) == tg.EINVAL and "x is NULL" in tg.last_error()
+    assert _q(16, 64, Q=None) == tg.EINVAL and "q is NULL" in tg.last_error()
+    assert _q(16, 64, S=None) == tg.EINVAL and "scales is NULL" in tg.last_error()
+    assert _q(16, 64, X=A16 + 4) == tg.EALIGN and "x is not 16-byte aligned" in tg.last_error()
+    assert _q(16, 64, Q=C16 + 8) == tg.EALIGN and "q is not 16-byte aligned" in tg.last_error()
+    assert _q(16, 64, Q=A16 + 64) == tg.EINVAL and "q overlaps x" in tg.last_error()
+    assert _q(16, 64, S=A16 + 3) == tg.EINVAL and "scales overlaps x" in tg.last_error()
+    assert _q(16, 64, S=C16 + 5) == tg.EINVAL and "scales overlaps q" in tg.last_error()
+    assert _q(1 << 31, 64) == tg.ETOOBIG

@@ -53,6 +53,9 @@ WORKLOADS = {
                  "bf16 NT GEMM M=4000 N=3000 K=5000 (ragged tails)"),
         Workload("mxfp8_nt_4096", "mxfp8_nt", 4096, 4096, 4096,
                  "block-scaled fp8 (e4m3 + e8m0 per 128 K) NT GEMM M=N=K=4096"),
+        # The step before the block-scaled GEMM: one of its operands, quantised.
+        Workload("quant_mxfp8_4096", "quant_mxfp8", 4096, 0, 4096,
+                 "block-scale quantiser fp32 -> e4m3fn + e8m0 per 128 K, M=K=4096"),
     )
 }
 
@@ -123,6 +126,8 @@ def make_random(kind: str, M: int, N: int, K: int, seed: int = 0):
     if kind == "f16_nn":
         return {"A": randn_bits((M, K), torch.float16, g),
                 "B": randn_bits((K, N), torch.float16, g)}
+    if kind == "quant_mxfp8":
+        return {"X": randn_f32((M, K), g).numpy()}
     if kind == "mxfp8_nt":
         a = randn_f32((M, K), g)
         b = randn_f32((N, K), g)
