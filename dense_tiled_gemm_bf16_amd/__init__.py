@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
     L.tgemm_set_tile.argtypes = [ctypes.c_int, ctypes.c_int]
     L.tgemm_set_tile.restype = ctypes.c_int
     L.quantize_mxfp8.argtypes = [i64, i64, p, p, p, p]
+    for f in (L.gemm_bf16, L.gemm_f16):
+        f.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64, p]
+        f.restype = ctypes.c_int
     L.quantize_mxfp8.restype = ctypes.c_int
     _lib = L
     return L
@@ -168,3 +171,45 @@ def quantize_mxfp8(x, q=None, scales=None, stream=None):
     scales = _out(scales, (M, KB), torch.uint8, x)
     check(lib().quantize_mxfp8(M, K, x.data_ptr(), q.data_ptr(), scales.data_ptr(), _stream_ptr(stream)))
     return q, scales
+
+
+def _layout(t, name):
+    """(transposed, leading dimension) of a 2-D tensor stored row-major
+    (stride (ld, 1)) or as the transpose of a row-major array (stride (1, ld))."""
+    r, c = t.shape
+    s0, s1 = t.stride()
+    if s1 == 1 and (s0 >= c or r == 1):
+        return 0, max(s0, c)
+    if s0 == 1 and (s1 >= r or c == 1):
+        return 1, max(s1, r)
+    raise ValueError(f"{name} must be row-major or a transposed row-major view (strides {t.stride()})")
+
+
+def gemm(a, b, out=None, stream=None):
+    """C = a @ b for 2-D bfloat16 or float16 CUDA tensors (gemm_bf16 / gemm_f16).
+
+    a (M,K) and b (K,N) may each be row-major with any row stride or the
+    transpose of such an array (e.g. ``x.t()``); out (M,N) row-major with
+    any row stride, allocated when None.  Output dtype = input dtype.
+    """
+    torch = _torch()
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not multiply")
+    if a.dtype != b.dtype or a.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("a and b must both be bfloat16 or both float16")
+    if a.device.type != "cuda" or b.device.type != "cuda":
+        raise ValueError("a and b must be on a GPU")
+    M, K = a.shape
+    N = b.shape[1]
+    ta, lda = _layout(a, "a")
+    # b is (K, N): row-major means B stored K x N (trans_b = 0); a transposed
+    # view means B stored N x K (trans_b = 1).
+    tb, ldb = _layout(b, "b")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if out.dtype != a.dtype or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1):
+        raise ValueError("out must be a row-major (M, N) tensor of the input dtype")
+    ldc = max(out.stride(0), N)
+    fn = lib().gemm_bf16 if a.dtype == torch.bfloat16 else lib().gemm_f16
+    check(fn(ta, tb, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, _stream_ptr(stream)))
+    return out

@@ -116,12 +116,70 @@ int dispatch(const char *fn, tgemm::Problem p) {
   if (rc != TGEMM_OK) return rc;
   p.tile_m = g_tile_m;
   p.tile_n = g_tile_n;
-  if (p.tile_m != 0 && !tgemm::shape_supported(p.kind, p.tile_m, p.tile_n))
+  if (p.tile_m != 0 && !tgemm::shape_supported(p, p.tile_m, p.tile_n))
     return fail(TGEMM_EINVAL, "%s: no %dx%d tile for this entry point (set by tgemm_set_tile)", fn, p.tile_m,
                 p.tile_n);
   hipError_t e = tgemm::launch(p);
   if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   return TGEMM_OK;
+}
+
+// C = op(A) op(B) for 16-bit inputs with any operand storage and row
+// strides (gemm_bf16 / gemm_f16).
+int gemm_general(const char *fn, tgemm::Dt dt, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                 const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
+  g_err[0] = '\0';
+  if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+    return fail(TGEMM_EINVAL, "%s: trans_a and trans_b must be 0 or 1 (got %d, %d)", fn, trans_a, trans_b);
+  if (M < 0 || N < 0 || K < 0)
+    return fail(TGEMM_EINVAL, "%s: negative size (M=%lld, N=%lld, K=%lld)", fn, (long long)M, (long long)N,
+                (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || lda > INT32_MAX || ldb > INT32_MAX || ldc > INT32_MAX)
+    return fail(TGEMM_ETOOBIG, "%s: sizes and strides must be below 2^31", fn);
+  if (M == 0 || N == 0) return TGEMM_OK;
+  // As stored: A is a_rows x a_cols, B is b_rows x b_cols.
+  const int64_t a_rows = trans_a ? K : M, a_cols = trans_a ? M : K;
+  const int64_t b_rows = trans_b ? N : K, b_cols = trans_b ? K : N;
+  if (lda < a_cols)
+    return fail(TGEMM_EINVAL, "%s: lda=%lld is below the stored row length of A (%lld)", fn, (long long)lda,
+                (long long)a_cols);
+  if (ldb < b_cols)
+    return fail(TGEMM_EINVAL, "%s: ldb=%lld is below the stored row length of B (%lld)", fn, (long long)ldb,
+                (long long)b_cols);
+  if (ldc < N)
+    return fail(TGEMM_EINVAL, "%s: ldc=%lld is below N=%lld", fn, (long long)ldc, (long long)N);
+  if (a_cols % 8 != 0)
+    return fail(TGEMM_EALIGN, "%s: %s=%lld (the contiguous dimension of A) must be a multiple of 8", fn,
+                trans_a ? "M" : "K", (long long)a_cols);
+  if (b_cols % 8 != 0)
+    return fail(TGEMM_EALIGN, "%s: %s=%lld (the contiguous dimension of B) must be a multiple of 8", fn,
+                trans_b ? "K" : "N", (long long)b_cols);
+  if (N % 8 != 0) return fail(TGEMM_EALIGN, "%s: N=%lld must be a multiple of 8", fn, (long long)N);
+  if (lda % 8 != 0 || ldb % 8 != 0 || ldc % 8 != 0)
+    return fail(TGEMM_EALIGN, "%s: lda, ldb and ldc must be multiples of 8 (got %lld, %lld, %lld)", fn,
+                (long long)lda, (long long)ldb, (long long)ldc);
+  if (!C) return fail(TGEMM_EINVAL, "%s: C is NULL", fn);
+  if (misaligned(C)) return fail(TGEMM_EALIGN, "%s: C is not 16-byte aligned", fn);
+  // Bytes each operand spans (nothing is read when K == 0).
+  const uint64_t a_bytes = K == 0 ? 0 : ((uint64_t)(a_rows - 1) * lda + a_cols) * 2;
+  const uint64_t b_bytes = K == 0 ? 0 : ((uint64_t)(b_rows - 1) * ldb + b_cols) * 2;
+  const uint64_t c_bytes = ((uint64_t)(M - 1) * ldc + N) * 2;
+  const Operand ops[] = {{"A", A, a_bytes, true}, {"B", B, b_bytes, true}};
+  for (const Operand &o : ops) {
+    if (o.bytes == 0) continue;
+    if (!o.ptr) return fail(TGEMM_EINVAL, "%s: %s is NULL", fn, o.name);
+    if (misaligned(o.ptr)) return fail(TGEMM_EALIGN, "%s: %s is not 16-byte aligned", fn, o.name);
+    if (overlaps(C, c_bytes, o.ptr, o.bytes)) return fail(TGEMM_EINVAL, "%s: C overlaps %s", fn, o.name);
+  }
+  // 31-bit buffer offsets: a K-contiguous operand is addressed per panel of
+  // 256 rows, an M/N-contiguous one as a whole.
+  const uint64_t a_span = trans_a ? a_bytes : (uint64_t)tgemm::kTileM * lda * 2;
+  const uint64_t b_span = trans_b ? (uint64_t)tgemm::kTileN * ldb * 2 : b_bytes;
+  if (a_span > kOffsetLimit) return fail(TGEMM_ETOOBIG, "%s: A too large for 31-bit offsets", fn);
+  if (b_span > kOffsetLimit) return fail(TGEMM_ETOOBIG, "%s: B too large for 31-bit offsets", fn);
+  tgemm::Problem p{dt, trans_a == 1, trans_b == 1, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream,
+                   0, 0, 0};
+  return dispatch(fn, p);
 }
 
 }  // namespace
@@ -134,6 +192,16 @@ int tgemm_init(void) {
 }
 
 const char *tgemm_last_error(void) { return g_err; }
+
+int gemm_bf16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+              const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
+  return gemm_general("gemm_bf16", tgemm::Dt::kBf16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+             const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
+  return gemm_general("gemm_f16", tgemm::Dt::kF16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
 
 int quantize_mxfp8(int64_t M, int64_t K, const float *x, void *q, void *scales, hipStream_t stream) {
   static const char fn[] = "quantize_mxfp8";
@@ -180,7 +248,7 @@ int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B, 
   if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
   if ((uint64_t)tgemm::kTileM * k * 2 > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
-  tgemm::Problem p{tgemm::Kind::kBf16NT, M, N, K, A, B, nullptr, nullptr, C, stream, 0, 0, 0};
+  tgemm::Problem p{tgemm::Dt::kBf16, false, true, M, N, K, A, K, B, K, nullptr, nullptr, C, N, stream, 0, 0, 0};
   return dispatch(fn, p);
 }
 
@@ -195,7 +263,7 @@ int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, v
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
   if (k * n * 2 > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: B too large (K * N * 2 bytes must stay below 2^31)", fn);
-  tgemm::Problem p{tgemm::Kind::kF16NN, M, N, K, A, B, nullptr, nullptr, C, stream, 0, 0, 0};
+  tgemm::Problem p{tgemm::Dt::kF16, false, false, M, N, K, A, K, B, N, nullptr, nullptr, C, N, stream, 0, 0, 0};
   return dispatch(fn, p);
 }
 
@@ -215,7 +283,7 @@ int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K bytes must stay below 2^31)", fn, (long long)K);
   if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
-  tgemm::Problem p{tgemm::Kind::kMxfp8NT, M, N, K, A, B, scale_A, scale_B, C, stream, 0, 0, 0};
+  tgemm::Problem p{tgemm::Dt::kMxfp8, false, true, M, N, K, A, K, B, K, scale_A, scale_B, C, N, stream, 0, 0, 0};
   return dispatch(fn, p);
 }
 

@@ -7,16 +7,23 @@
 
 namespace tgemm {
 
-enum class Kind : int { kBf16NT = 0, kF16NN = 1, kMxfp8NT = 2 };
+// Element type of A and B (C is bf16, or fp16 for fp16 inputs).
+enum class Dt : int { kBf16 = 0, kF16 = 1, kMxfp8 = 2 };
 
-// A validated problem: sizes are non-negative and fit the kernels' limits,
-// pointers are aligned, M > 0 and N > 0.
+// A validated problem, C = op(A) op(B): sizes are non-negative and fit the
+// kernels' limits, pointers and row strides are aligned, M > 0 and N > 0.
 struct Problem {
-  Kind kind;
+  Dt dt;
+  bool trans_a;  // A is stored K x M (op(A) = A^T); else M x K
+  bool trans_b;  // B is stored N x K (op(B) = B^T); else K x N
   int64_t M, N, K;
-  const void *A, *B;
+  const void *A;
+  int64_t lda;  // row stride of A as stored, in elements
+  const void *B;
+  int64_t ldb;
   const void *scale_A, *scale_B;  // mxfp8 only
   void *C;
+  int64_t ldc;
   hipStream_t stream;
   int cus;             // compute units of the device
   int tile_m, tile_n;  // forced output tile, or 0, 0 to choose by shape
@@ -30,8 +37,8 @@ constexpr int kTileN = 256;
 // (hipErrorInvalidValue for a forced tile the kind does not have).
 hipError_t launch(const Problem &p);
 
-// Whether `kind` has a kernel for output tiles of tile_m x tile_n.
-bool shape_supported(Kind kind, int tile_m, int tile_n);
+// Whether p's element type and layout have a kernel for tile_m x tile_n tiles.
+bool shape_supported(const Problem &p, int tile_m, int tile_n);
 
 // A validated block-scale quantisation: M, K > 0, K % 16 == 0, x and q
 // 16-byte aligned.

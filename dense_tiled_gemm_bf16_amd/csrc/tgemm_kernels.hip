@@ -35,8 +35,12 @@
 //    and, for the block-scaled path, v_mfma_scale_f32_32x32x64_f8f6f4
 //    (4 x 4 blocks) with the e8m0 block scales as operands (TCGEN05
 //    tutorial, "进阶" (Advanced)).
-//  * NN: B stays K x N in LDS and is read with the LDS transpose read
-//    (ds_read_b64_tr_b16), which hands each lane four K values of one column.
+//  * operand layouts (trans_A / trans_B of the SM100 README's T.gemm): an
+//    operand stored K-contiguous (A as M x K, B as N x K) is staged row by
+//    row as above; one stored M- or N-contiguous (A as K x M, B as K x N)
+//    stays K-major in LDS and is read with the LDS transpose read
+//    (ds_read_b64_tr_b16), which hands each lane four K values of one
+//    column.  Rows of every operand and of C are ld elements apart.
 //  * epilogue: fp32 -> bf16/fp16 with round-to-nearest-even, masked stores.
 //    The MFMA is fed B rows as its first operand and A rows as its second,
 //    so each lane's accumulators hold 4 consecutive columns of one row of C
@@ -77,27 +81,21 @@ struct Args {
   const uint8_t *SB;
   uint8_t *C;
   int M, N, K;
+  int lda, ldb, ldc;  // row strides of A, B and C as stored, in elements
   int tiles_m, tiles_n;
   int ksteps;  // ceil(K / elements per slice)
   int kb;      // scale blocks per row (mxfp8)
 };
 
-template <int KIND>
-struct Traits;
-template <>
-struct Traits<0> {  // bf16 NT
-  static constexpr int kElem = 2;
-  static constexpr bool kNN = false, kScaled = false;
-};
-template <>
-struct Traits<1> {  // fp16 NN
-  static constexpr int kElem = 2;
-  static constexpr bool kNN = true, kScaled = false;
-};
-template <>
-struct Traits<2> {  // mxfp8 NT
-  static constexpr int kElem = 1;
-  static constexpr bool kNN = false, kScaled = true;
+// Element type of A and B, and the storage of each: AK, A is M x K
+// (K-contiguous; else K x M); BK, B is N x K (K-contiguous; else K x N).
+enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2 };
+template <int DT, bool AK, bool BK>
+struct Traits {
+  static constexpr int kDt = DT;
+  static constexpr int kElem = DT == kFp8 ? 1 : 2;
+  static constexpr bool kAK = AK, kBK = BK;
+  static constexpr bool kScaled = DT == kFp8;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -177,15 +175,15 @@ struct PanelLoader {
   uint32_t off[NI];  // per instruction: byte offset of this lane's chunk at slice 0
   int kcol[2];       // element column of this lane's chunk inside a slice (even / odd i)
 
-  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int elem, int wave,
+  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int ld, int elem, int wave,
                                        int lane) {
-    rsrc = make_rsrc(panel, (uint32_t)rows_valid * (uint32_t)K * (uint32_t)elem);
+    rsrc = make_rsrc(panel, ((uint32_t)(rows_valid - 1) * (uint32_t)ld + (uint32_t)K) * (uint32_t)elem);
 #pragma unroll
     for (int p = 0; p < 2; ++p) kcol[p] = ((lane & 7) ^ swz(8 * p + (lane >> 3))) * (16 / elem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = wave * 8 * NI + i * 8 + (lane >> 3);
-      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem : kOOB;
+      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)ld * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem : kOOB;
     }
   }
 
@@ -199,33 +197,34 @@ struct PanelLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Staging of one K slice of the NN B operand (K x N, N-contiguous) for a
-// tile of TN columns into a slot of 64 K rows x 2 TN bytes.  Wave w moves K
-// rows [16 w, 16 w + 16) with NI = TN / 32 instructions of RPI = 512 / TN
+// Staging of one K slice of an M- or N-contiguous 16-bit operand (A stored
+// K x M, B stored K x N, rows ld elements apart) for a tile of W columns
+// (W = 256 or 128) into a slot of 64 K rows x 2 W bytes.  Wave w moves K
+// rows [16 w, 16 w + 16) with NI = W / 32 instructions of RPI = 512 / W
 // rows each; lane l of instruction i writes row 16 w + RPI i + l / LPR
-// (LPR = TN / 8 lanes per row), physical chunk l % LPR, fetching logical
-// chunk (l % LPR) ^ swz_nn(row), i.e. columns n0 + 8 chunk .. + 8.
+// (LPR = W / 8 lanes per row), physical chunk l % LPR, fetching logical
+// chunk (l % LPR) ^ swz_nn(row), i.e. columns c0 + 8 chunk .. + 8.
 // ---------------------------------------------------------------------------
-template <int TN>
-struct NNLoader {
-  // (Instantiated, unused, for the NT kinds' other widths; the NN kernels
-  // use TN = 256 or 128, where an instruction covers whole rows.)
-  static constexpr int NI = TN / 32, RPI = 512 / TN, LPR = TN / 8;
+template <int W>
+struct MNLoader {
+  static_assert(W == 256 || W == 128, "an instruction covers whole K rows of the slot");
+  static constexpr int NI = W / 32, RPI = 512 / W, LPR = W / 8;
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[NI];  // per instruction: byte offset at slice 0 (kOOB past N)
+  uint32_t off[NI];  // per instruction: byte offset at slice 0 (kOOB past the last column)
   int krow0;         // K row of instruction 0 inside the slice
   uint32_t slice_bytes;
 
-  __device__ __forceinline__ void init(const uint8_t *B, int K, int N, int n0, int wave, int lane) {
-    rsrc = make_rsrc(B, (uint32_t)K * (uint32_t)N * 2u);
-    const uint32_t row_bytes = (uint32_t)N * 2u;
+  // X: the whole operand; ext: its columns (M or N); c0: the tile's first.
+  __device__ __forceinline__ void init(const uint8_t *X, int K, int ext, int c0, int ld, int wave, int lane) {
+    rsrc = make_rsrc(X, K > 0 ? ((uint32_t)(K - 1) * (uint32_t)ld + (uint32_t)ext) * 2u : 0u);
+    const uint32_t row_bytes = (uint32_t)ld * 2u;
     slice_bytes = 64u * row_bytes;
     krow0 = wave * 16 + lane / LPR;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int kr = krow0 + RPI * i;
-      const int n = n0 + ((lane % LPR) ^ swz_nn(kr)) * 8;
-      off[i] = n < N ? (uint32_t)kr * row_bytes + (uint32_t)n * 2u : kOOB;
+      const int c = c0 + ((lane % LPR) ^ swz_nn(kr)) * 8;
+      off[i] = c < ext ? (uint32_t)kr * row_bytes + (uint32_t)c * 2u : kOOB;
     }
   }
 
@@ -245,12 +244,11 @@ struct Slots {
   LDS_AS uint8_t *junk;  // 256 bytes per wave: landing area of the L2 prefetches
 };
 
-template <int KIND, int TM, int TN>
+template <class T, int TM, int TN>
 struct Kernel {
-  using T = Traits<KIND>;
   static constexpr int kElem = T::kElem;
   static constexpr int kWM = TM / 2, kWN = TN / 2;   // wave tile (2 x 2 waves)
-  static constexpr int kSlotA = TM * kRowBytes;      // one slot of A, of B (NN: 64 K rows x 2 TN bytes)
+  static constexpr int kSlotA = TM * kRowBytes;      // one slot of A, of B (K-major: 64 K rows x 2 TM / 2 TN bytes)
   static constexpr int kSlotB = TN * kRowBytes;
   static constexpr int kSliceK = kRowBytes / kElem;  // K elements per slice
   // MFMA shape.  16-bit inputs: v_mfma_f32_16x16x32 (it reads and writes 4
@@ -267,8 +265,8 @@ struct Kernel {
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
   static constexpr int kLA = TM / 32, kLB = TN / 32;  // load instructions per wave per slice
   static constexpr int kLoads = kLA + kLB;
-  static_assert(!T::kScaled || (TM == 256 && TN == 256), "the block-scaled kernel uses 256 x 256 tiles");
-  static_assert(!T::kNN || TN == 256 || TN == 128, "NN tiles are 256 or 128 columns wide");
+  static_assert(!T::kScaled || (TM == 256 && TN == 256 && T::kAK && T::kBK),
+                "the block-scaled kernel uses 256 x 256 tiles of K-contiguous operands");
   static_assert(kWM % kBlk == 0 && kWN % kBlk == 0, "wave tile");
   // Schedule, in MFMAs of a slice: the wait + barrier go before MFMA
   // kBarrierAt; the 16 loads of slice kt + 2 go out evenly over the kWindow
@@ -333,9 +331,8 @@ struct Kernel {
   int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
-  PanelLoader<kLA> la;
-  PanelLoader<kLB> lb;
-  NNLoader<TN> lnn;
+  typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type la;
+  typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type lb;
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
   // Block scales (fp8).  They are fetched once per group of 4 slices: a
@@ -376,10 +373,13 @@ struct Kernel {
     }
   }
 
-  // NN x fragment: columns n = col0 + l % 16 of the [k][n] B slot, K values
-  // 32 sub + 8 (l / 16) + 0..7.  Each transpose read gives a lane 4 K values
-  // of one column: in a 16-lane group, source lane 4 e + q points at K row
-  // base + e, columns col0 + 4 q .. + 3, and lane i receives column col0 + i.
+  // Fragment of 16 columns col0 + l % 16 of a K-major slot W columns wide
+  // (the [k][n] B slot, or the [k][m] A slot), K values 32 sub + 8 (l / 16)
+  // + 0..7: the same lane layout as read_rows gives.  Each transpose read
+  // gives a lane 4 K values of one column: in a 16-lane group, source lane
+  // 4 e + q points at K row base + e, columns col0 + 4 q .. + 3, and lane i
+  // receives column col0 + i.
+  template <int W>
   __device__ __forceinline__ Frag read_cols(const LDS_AS uint8_t *slot, int col0, int sub) const {
     const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
     const int n = col0 + 4 * q;
@@ -389,7 +389,7 @@ struct Kernel {
       const int kr = 32 * sub + 8 * g + 4 * t + e;
       // (Masked to the slot so the compiler can see the read stays inside it
       // and needs no wait for loads into the other slot.)
-      const int off = (kr * (2 * TN) + (((n >> 3) ^ swz_nn(kr)) << 4) + (n & 7) * 2) & (kSlotB - 1);
+      const int off = (kr * (2 * W) + (((n >> 3) ^ swz_nn(kr)) << 4) + (n & 7) * 2) & (W * kRowBytes - 1);
       const LDS_AS uint8_t *p = slot + off;
       s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)p);
       u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -409,14 +409,14 @@ struct Kernel {
     // compiler still places the LDS waits for the fragment inputs; the
     // accumulators are never written by VALU code and are read by it only
     // after fence_acc().
-    if constexpr (KIND == 0) {
+    if constexpr (T::kDt == kBf16) {
       Acc d = c;
       if constexpr (FIRST)
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(d) : "v"(x), "v"(y));
       else
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
       return d;
-    } else if constexpr (KIND == 1) {
+    } else if constexpr (T::kDt == kF16) {
       Acc d = c;
       if constexpr (FIRST)
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(d) : "v"(x), "v"(y));
@@ -446,12 +446,15 @@ struct Kernel {
   template <int S, int R>
   __device__ __forceinline__ void read_one(Frags &f, int sub) const {
     if constexpr (R < kNBn) {
-      if constexpr (T::kNN)
-        f.x[R] = read_cols(slots.b[S], wave_n * kWN + R * kBlk, sub);
-      else
+      if constexpr (T::kBK)
         f.x[R] = read_rows(slots.b[S], wave_n * kWN + R * kBlk, sub);
+      else
+        f.x[R] = read_cols<TN>(slots.b[S], wave_n * kWN + R * kBlk, sub);
     } else {
-      f.y[R - kNBn] = read_rows(slots.a[S], wave_m * kWM + (R - kNBn) * kBlk, sub);
+      if constexpr (T::kAK)
+        f.y[R - kNBn] = read_rows(slots.a[S], wave_m * kWM + (R - kNBn) * kBlk, sub);
+      else
+        f.y[R - kNBn] = read_cols<TM>(slots.a[S], wave_m * kWM + (R - kNBn) * kBlk, sub);
     }
   }
 
@@ -465,11 +468,15 @@ struct Kernel {
   template <int S>
   __device__ __forceinline__ void load_one(int kt, int i) {
     if (i < kLA) {
-      la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
-    } else if constexpr (T::kNN) {
-      lnn.issue(slots.b[S], wave, kt, a.K, i - kLA);
+      if constexpr (T::kAK)
+        la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
+      else
+        la.issue(slots.a[S], wave, kt, a.K, i);
     } else {
-      lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
+      if constexpr (T::kBK)
+        lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
+      else
+        lb.issue(slots.b[S], wave, kt, a.K, i - kLA);
     }
   }
 
@@ -571,11 +578,14 @@ struct Kernel {
     const int K = a.K;
     nk = a.ksteps;
 
-    la.init(a.A + (size_t)m0 * K * kElem, min(a.M - m0, TM), K, kElem, wave, lane);
-    if constexpr (T::kNN)
-      lnn.init(a.B, K, a.N, n0, wave, lane);
+    if constexpr (T::kAK)
+      la.init(a.A + (size_t)m0 * a.lda * kElem, min(a.M - m0, TM), K, a.lda, kElem, wave, lane);
     else
-      lb.init(a.B + (size_t)n0 * K * kElem, min(a.N - n0, TN), K, kElem, wave, lane);
+      la.init(a.A, K, a.M, m0, a.lda, wave, lane);
+    if constexpr (T::kBK)
+      lb.init(a.B + (size_t)n0 * a.ldb * kElem, min(a.N - n0, TN), K, a.ldb, kElem, wave, lane);
+    else
+      lb.init(a.B, K, a.N, n0, a.ldb, wave, lane);
     if constexpr (kPfDist > 0) {
       // Waves 0-1 take 32 rows of the A panel (its share among the 8 tile
       // columns of an XCD's block), waves 2-3 take 64 rows of the B panel
@@ -585,7 +595,7 @@ struct Kernel {
       const int rows_valid = is_a ? min(a.M - m0, TM) : min(a.N - n0, TN);
       const int r = is_a ? 32 * (tn & 7) + 16 * wave + (lane & 15) : 64 * (tm & 3) + 32 * (wave - 2) + (lane & 31);
       const bool active = is_a ? lane < 16 : lane < 32;
-      pf_off = active && r < rows_valid ? (uint32_t)r * (uint32_t)K * (uint32_t)kElem : kOOB;
+      pf_off = active && r < rows_valid ? (uint32_t)r * (uint32_t)(is_a ? a.lda : a.ldb) * (uint32_t)kElem : kOOB;
     }
     if constexpr (T::kScaled) {
       // Each operand's scale rows of this tile through a resource based at
@@ -670,7 +680,7 @@ struct Kernel {
     for (int j = 0; j < kNBm; ++j) {
       const int m = m0 + wave_m * kWM + j * kBlk + row_l;
       if (m >= a.M) continue;
-      uint8_t *crow = a.C + (size_t)m * a.N * 2;
+      uint8_t *crow = a.C + (size_t)m * a.ldc * 2;
 #pragma unroll
       for (int i = 0; i < kNBn; ++i) {
 #pragma unroll
@@ -680,7 +690,7 @@ struct Kernel {
           const f32x2 lo = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]};
           const f32x2 up = {acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           u32x2 pk;
-          if constexpr (KIND == 1) {
+          if constexpr (T::kDt == kF16) {
             pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2));
             pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(up, f16x2));
           } else {
@@ -700,7 +710,7 @@ struct Kernel {
 template <int TM, int TN>
 constexpr int kWgPerCu = TM * TN <= 128 * 128 ? 2 : 1;
 
-template <int KIND, int TM, int TN>
+template <class T, int TM, int TN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWgPerCu<TM, TN>, kWgPerCu<TM, TN>)))
 void gemm_kernel(const Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body is device code only; the host pass needs the symbol
@@ -718,18 +728,39 @@ void gemm_kernel(const Args a) {
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
   slots.junk = (LDS_AS uint8_t *)junk;
-  Kernel<KIND, TM, TN> k(a, slots);
+  Kernel<T, TM, TN> k(a, slots);
   k.run();
 #endif
 }
 
-template <int KIND, int TM, int TN>
+template <class T, int TM, int TN>
 hipError_t launch_shape(const Problem &p, Args a) {
   a.tiles_m = (int)((p.M + TM - 1) / TM);
   a.tiles_n = (int)((p.N + TN - 1) / TN);
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
-  hipLaunchKernelGGL((gemm_kernel<KIND, TM, TN>), grid, block, 0, p.stream, a);
+  hipLaunchKernelGGL((gemm_kernel<T, TM, TN>), grid, block, 0, p.stream, a);
   return hipGetLastError();
+}
+
+// The 16-bit kernels of one operand layout, by tile shape (256 x 192 only
+// where B is K-contiguous: a K-major B slot must be 256 or 128 wide).
+template <int DT, bool AK, bool BK>
+hipError_t launch_layout(const Problem &p, const Args &a, int tm, int tn) {
+  using T = Traits<DT, AK, BK>;
+  if (tm == 256 && tn == 256) return launch_shape<T, 256, 256>(p, a);
+  if constexpr (BK)
+    if (tm == 256 && tn == 192) return launch_shape<T, 256, 192>(p, a);
+  if (tm == 128 && tn == 128) return launch_shape<T, 128, 128>(p, a);
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_dt(const Problem &p, const Args &a, int tm, int tn) {
+  const bool ak = !p.trans_a, bk = p.trans_b;
+  if (ak && bk) return launch_layout<DT, true, true>(p, a, tm, tn);
+  if (ak) return launch_layout<DT, true, false>(p, a, tm, tn);
+  if (bk) return launch_layout<DT, false, true>(p, a, tm, tn);
+  return launch_layout<DT, false, false>(p, a, tm, tn);
 }
 
 // Tile shapes per kind, largest first, each with a rate relative to
@@ -744,8 +775,8 @@ struct Shape {
   int tm, tn;
   double rel;
 };
-constexpr Shape kShapesNT[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.45}};
-constexpr Shape kShapesNN[] = {{256, 256, 1.0}, {128, 128, 0.45}};
+constexpr Shape kShapesBK[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.45}};  // B K-contiguous
+constexpr Shape kShapesBN[] = {{256, 256, 1.0}, {128, 128, 0.45}};                     // B N-contiguous
 
 // The shape with the least estimated time: whole waves of tiles over the
 // CUs, each wave costing its tile area over the shape's relative rate.
@@ -779,44 +810,37 @@ hipError_t launch(const Problem &p) {
   a.M = (int)p.M;
   a.N = (int)p.N;
   a.K = (int)p.K;
-  const int slice = p.kind == Kind::kMxfp8NT ? 128 : 64;
+  a.lda = (int)p.lda;
+  a.ldb = (int)p.ldb;
+  a.ldc = (int)p.ldc;
+  const int slice = p.dt == Dt::kMxfp8 ? 128 : 64;
   a.ksteps = (int)((p.K + slice - 1) / slice);
   a.kb = (int)((p.K + 127) / 128);
   int tm = p.tile_m, tn = p.tile_n;
   if (tm == 0) {
-    const Shape s = p.kind == Kind::kBf16NT  ? pick_shape(kShapesNT, p.M, p.N, p.cus)
-                    : p.kind == Kind::kF16NN ? pick_shape(kShapesNN, p.M, p.N, p.cus)
-                                             : Shape{256, 256, 1.0};
+    const Shape s = p.dt == Dt::kMxfp8 ? Shape{256, 256, 1.0}
+                    : p.trans_b        ? pick_shape(kShapesBK, p.M, p.N, p.cus)
+                                       : pick_shape(kShapesBN, p.M, p.N, p.cus);
     tm = s.tm;
     tn = s.tn;
   }
-  switch (p.kind) {
-    case Kind::kBf16NT:
-      if (tm == 256 && tn == 256) return launch_shape<0, 256, 256>(p, a);
-      if (tm == 256 && tn == 192) return launch_shape<0, 256, 192>(p, a);
-      if (tm == 128 && tn == 128) return launch_shape<0, 128, 128>(p, a);
-      break;
-    case Kind::kF16NN:
-      if (tm == 256 && tn == 256) return launch_shape<1, 256, 256>(p, a);
-      if (tm == 128 && tn == 128) return launch_shape<1, 128, 128>(p, a);
-      break;
-    case Kind::kMxfp8NT:
-      if (tm == 256 && tn == 256) return launch_shape<2, 256, 256>(p, a);
+  switch (p.dt) {
+    case Dt::kBf16:
+      return launch_dt<kBf16>(p, a, tm, tn);
+    case Dt::kF16:
+      return launch_dt<kF16>(p, a, tm, tn);
+    case Dt::kMxfp8:
+      if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
+        return launch_shape<Traits<kFp8, true, true>, 256, 256>(p, a);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-bool shape_supported(Kind kind, int tile_m, int tile_n) {
-  switch (kind) {
-    case Kind::kBf16NT:
-      return (tile_m == 256 && (tile_n == 256 || tile_n == 192)) || (tile_m == 128 && tile_n == 128);
-    case Kind::kF16NN:
-      return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128);
-    case Kind::kMxfp8NT:
-      return tile_m == 256 && tile_n == 256;
-  }
-  return false;
+bool shape_supported(const Problem &p, int tile_m, int tile_n) {
+  if (p.dt == Dt::kMxfp8) return tile_m == 256 && tile_n == 256;
+  return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128) ||
+         (tile_m == 256 && tile_n == 192 && p.trans_b);
 }
 
 }  // namespace tgemm

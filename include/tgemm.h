@@ -116,6 +116,40 @@ TGEMM_API int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K,
                   void *C, hipStream_t stream);
 
 /*
+ * C = op(A) . op(B) for 16-bit inputs with any operand storage and row
+ * strides: bfloat16 in and out (gemm_bf16), fp16 in and out (gemm_f16);
+ * fp32 accumulation.
+ *
+ * The pages' GEMM takes transpose flags for its operands (TileLang SM100
+ * README, "Code Example": T.gemm(..., trans_B=True); the tutorial notes
+ * trans_A as well) and addresses its tensors through row strides (velog
+ * "tilelang", 1.2 Pass Pipeline, Host IRModule).
+ *
+ *   trans_a  0: A is stored M x K (op(A) = A);   1: A is stored K x M (op(A) = A^T)
+ *   trans_b  0: B is stored K x N (op(B) = B);   1: B is stored N x K (op(B) = B^T)
+ *   A, B     device pointers, row-major as stored, rows lda / ldb elements apart
+ *   C        device pointer, M x N row-major, rows ldc elements apart;
+ *            written (only its M x N elements), never read
+ *
+ * Each output is the fp32 sum over k of op(A)[m][k] * op(B)[k][n], rounded
+ * to nearest-even bf16 (fp16 for gemm_f16, overflow to +-inf).  K == 0
+ * writes zeros.  gemm_bf16(0, 1, ...) with packed strides is gemm_bf16_nt;
+ * gemm_f16(0, 0, ...) with packed strides is gemm_f16_nn.
+ * Requirements: trans_a, trans_b in {0, 1}; lda, ldb, ldc at least the
+ * stored row lengths and multiples of 8; the contiguous dimension of each
+ * stored operand (K or M for A, N or K for B) and N multiples of 8; A, B
+ * and C 16-byte aligned and C not overlapping A or B; a K-contiguous
+ * operand's 256 rows and an M/N-contiguous operand as a whole below 2^31
+ * bytes.
+ */
+TGEMM_API int gemm_bf16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda, const void *B, int64_t ldb,
+                        void *C, int64_t ldc, hipStream_t stream);
+TGEMM_API int gemm_f16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, const void *B, int64_t ldb,
+                       void *C, int64_t ldc, hipStream_t stream);
+
+/*
  * Block-scale quantiser: binary32 rows to the operand format of
  * gemm_mxfp8_nt (the step before the block-scaled GEMM; one scale per 128 K
  * elements as in the Blackwell TCGEN05 GEMM tutorial, section "进阶"
@@ -160,8 +194,8 @@ TGEMM_API const char *tgemm_last_error(void);
  * fewest waves of workgroups for the least work (the pages' kernels take
  * their block sizes as parameters: SM100 README, "Code Example",
  * block_M / block_N; velog "tilelang", 1.1 Front-End DSL).
- *   gemm_bf16_nt:  256x256, 256x192, 128x128
- *   gemm_f16_nn:   256x256, 128x128
+ *   B stored N x K (gemm_bf16_nt, trans_b = 1): 256x256, 256x192, 128x128
+ *   B stored K x N (gemm_f16_nn, trans_b = 0):  256x256, 128x128
  *   gemm_mxfp8_nt: 256x256
  * Returns TGEMM_OK, or TGEMM_EINVAL for a shape no entry point has; an
  * entry point called with a shape it does not have returns TGEMM_EINVAL.

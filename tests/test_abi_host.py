@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "quantize_mxfp8", "tgemm_init", "tgemm_last_error",
-         "tgemm_set_tile"])
+        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
+         "tgemm_last_error", "tgemm_set_tile"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -169,3 +169,33 @@ def test_quantize_validation():
     assert _q(16, 64, S=A16 + 3) == tg.EINVAL and "scales overlaps x" in tg.last_error()
     assert _q(16, 64, S=C16 + 5) == tg.EINVAL and "scales overlaps q" in tg.last_error()
     assert _q(1 << 31, 64) == tg.ETOOBIG
+
+
+def _g(ta, tb, M, N, K, lda, ldb, ldc, A=A16, B=B16, C=C16, fn="gemm_bf16"):
+    return getattr(tg.lib(), fn)(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_bf16", "gemm_f16"])
+def test_general_entry_validation(fn):
+    assert _g(0, 0, 0, 16, 16, 16, 16, 16, A=None, B=None, C=None, fn=fn) == tg.OK
+    assert _g(2, 0, 16, 16, 16, 16, 16, 16, fn=fn) == tg.EINVAL and "0 or 1" in tg.last_error()
+    assert _g(0, 0, -1, 16, 16, 16, 16, 16, fn=fn) == tg.EINVAL and "negative size" in tg.last_error()
+    # Strides below the stored row length: A M x K (lda >= K), A K x M (lda >= M), ...
+    assert _g(0, 0, 32, 16, 64, 48, 16, 16, fn=fn) == tg.EINVAL and "lda=48" in tg.last_error()
+    assert _g(1, 0, 32, 16, 64, 24, 16, 16, fn=fn) == tg.EINVAL and "lda=24" in tg.last_error()
+    assert _g(0, 0, 32, 16, 64, 64, 8, 16, fn=fn) == tg.EINVAL and "ldb=8" in tg.last_error()
+    assert _g(0, 1, 32, 16, 64, 64, 32, 16, fn=fn) == tg.EINVAL and "ldb=32" in tg.last_error()
+    assert _g(0, 0, 32, 16, 64, 64, 16, 8, fn=fn) == tg.EINVAL and "ldc=8" in tg.last_error()
+    # Vector width: the contiguous dimension of each stored operand, N, and the strides.
+    assert _g(0, 0, 32, 16, 60, 64, 16, 16, fn=fn) == tg.EALIGN and "contiguous dimension of A" in tg.last_error()
+    assert _g(1, 0, 30, 16, 64, 32, 16, 16, fn=fn) == tg.EALIGN and "M=30" in tg.last_error()
+    assert _g(0, 1, 32, 16, 60, 64, 64, 16, fn=fn) == tg.EALIGN
+    assert _g(0, 0, 32, 12, 64, 64, 16, 16, fn=fn) == tg.EALIGN
+    assert _g(0, 0, 32, 16, 64, 68, 16, 16, fn=fn) == tg.EALIGN and "multiples of 8" in tg.last_error()
+    # Pointers and overlap.
+    assert _g(0, 0, 32, 16, 64, 64, 16, 16, A=A16 + 2, fn=fn) == tg.EALIGN and "A is not" in tg.last_error()
+    assert _g(0, 0, 32, 16, 64, 64, 16, 16, C=None, fn=fn) == tg.EINVAL and "C is NULL" in tg.last_error()
+    assert _g(0, 0, 32, 16, 64, 64, 16, 16, C=A16 + 64, fn=fn) == tg.EINVAL and "C overlaps A" in tg.last_error()
+    # 31-bit offsets: an M-contiguous A addressed as a whole.
+    far = 0x7F0000000000
+    assert _g(1, 0, 1 << 16, 16, 1 << 15, 1 << 16, 16, 16, C=far, fn=fn) == tg.ETOOBIG
