@@ -66,6 +66,11 @@ def _load():
     for name in ("oracle_encode_bf16", "oracle_encode_f16"):
         getattr(lib, name).argtypes = [i64, f64p, u16p]
     lib.oracle_encode_e4m3fn.argtypes = [i64, f64p, u8p]
+    lib.oracle_decode_e2m1.argtypes = [i64, u8p, f64p]
+    lib.oracle_gemm_mxfp4_nt.argtypes = [i64, i64, i64, u8p, u8p, u8p, u8p, u16p, f64p]
+    lib.oracle_gemm_mxfp4_nt.restype = None
+    lib.oracle_gemm_mxfp4_nt_at.argtypes = [i64, i64, i64, u8p, u8p, u8p, u8p, i64, i64p, i64p, u16p, f64p]
+    lib.oracle_gemm_mxfp4_nt_at.restype = None
     lib.oracle_quantize_mxfp8.argtypes = [i64, i64, ctypes.c_void_p, u8p, u8p]
     lib.oracle_quantize_mxfp8.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -256,4 +261,53 @@ def gemm_mxfp8_nt_at(qA, qB, sA, sB, rows, cols, want_f64: bool = False):
     _load().oracle_gemm_mxfp8_nt_at(M, N, K, _ptr(qA), _ptr(qB), _ptr(sA), _ptr(sB),
                                     rows.size, _ptr(rows), _ptr(cols), _ptr(out),
                                     _ptr(out64))
+    return (out, out64) if want_f64 else out
+
+
+# --- MXFP4 ---------------------------------------------------------------------
+
+def decode_e2m1(nibbles) -> np.ndarray:
+    """FP4 E2M1 codes (0..15, one per byte) -> float64."""
+    b = _c(np.asarray(nibbles, np.uint8), np.uint8)
+    out = np.empty(b.shape, np.float64)
+    _load().oracle_decode_e2m1(b.size, _ptr(b), _ptr(out))
+    return out
+
+
+def _mxfp4_shapes(qA, qB, sA, sB, K):
+    (M, KH), (N, KH2) = qA.shape, qB.shape
+    if K is None:
+        K = 2 * KH
+    KB = (K + 31) // 32
+    if KH != (K + 1) // 2 or KH2 != KH or sA.shape != (M, KB) or sB.shape != (N, KB):
+        raise ValueError("operand shapes do not match")
+    return M, N, K
+
+
+def gemm_mxfp4_nt(qA, qB, sA, sB, K=None, want_f64: bool = False):
+    """Block-scaled FP4 NT GEMM -> C (M,N) bf16 bits.
+
+    qA (M,K/2), qB (N,K/2): E2M1 elements packed two per byte (element 2i in
+    the low nibble of byte i); sA (M,ceil(K/32)), sB (N,ceil(K/32)): e8m0
+    bytes, one per row per 32 K elements.
+    """
+    qA, qB, sA, sB = (_c(x, np.uint8) for x in (qA, qB, sA, sB))
+    M, N, K = _mxfp4_shapes(qA, qB, sA, sB, K)
+    C = np.empty((M, N), np.uint16)
+    C64 = np.empty((M, N), np.float64) if want_f64 else None
+    _load().oracle_gemm_mxfp4_nt(M, N, K, _ptr(qA), _ptr(qB), _ptr(sA), _ptr(sB), _ptr(C), _ptr(C64))
+    return (C, C64) if want_f64 else C
+
+
+def gemm_mxfp4_nt_at(qA, qB, sA, sB, rows, cols, K=None, want_f64: bool = False):
+    """C[rows[p], cols[p]] of the block-scaled FP4 NT GEMM (bf16 bits)."""
+    qA, qB, sA, sB = (_c(x, np.uint8) for x in (qA, qB, sA, sB))
+    M, N, K = _mxfp4_shapes(qA, qB, sA, sB, K)
+    rows, cols = _points(rows, cols)
+    if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+        raise ValueError("bad sample positions")
+    out = np.empty(rows.size, np.uint16)
+    out64 = np.empty(rows.size, np.float64) if want_f64 else None
+    _load().oracle_gemm_mxfp4_nt_at(M, N, K, _ptr(qA), _ptr(qB), _ptr(sA), _ptr(sB), rows.size,
+                                    _ptr(rows), _ptr(cols), _ptr(out), _ptr(out64))
     return (out, out64) if want_f64 else out

@@ -86,6 +86,27 @@ double oracle_e4m3fn_to_f64(uint8_t b)
     return sign ? -v : v;
 }
 
+/*
+ * OCP FP4 E2M1 (the MXFP4 element type): sign, 2 exponent bits (bias 1),
+ * 1 mantissa bit; exponent 0 is subnormal (0 or 0.5); no infinities or
+ * NaN.  Values: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives.
+ */
+double oracle_e2m1_to_f64(uint8_t nibble)
+{
+    int sign = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 3;
+    int f = nibble & 1;
+    double v = e == 0 ? 0.5 * f : ldexp(1.0 + 0.5 * f, e - 1);
+    return sign ? -v : v;
+}
+
+/* Element k of a row of packed FP4: byte k / 2, the low nibble for even k. */
+static uint8_t fp4_at(const uint8_t *row, int64_t k)
+{
+    uint8_t b = row[k / 2];
+    return (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+}
+
 /* OCP E8M0 scale: an unsigned biased exponent, value 2^(E-127); 0xFF is NaN. */
 double oracle_e8m0_to_f64(uint8_t e)
 {
@@ -338,6 +359,39 @@ void oracle_gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K,
 }
 
 /*
+ * MXFP4 NT: C[m][n] = R_bf16( sum_k (e2m1(A[m][k]) * 2^(EA[m][k/32]-127))
+ *                                  * (e2m1(B[n][k]) * 2^(EB[n][k/32]-127)) ).
+ * Block-scaled formats other than MXFP8 (Blackwell TCGEN05 GEMM tutorial,
+ * section "进阶" (Advanced), names MXFP8 "and other" block-scaled formats);
+ * the pages give the FP4 layout and block size of none, so this follows the
+ * OCP MX format: E2M1 elements packed two per byte, element 2i in the low
+ * nibble of byte i, and one E8M0 scale per 32 consecutive elements along K.
+ * A row of qA holds K/2 bytes; sA is M x ceil(K/32).
+ */
+void oracle_gemm_mxfp4_nt(int64_t M, int64_t N, int64_t K,
+                          const uint8_t *qA, const uint8_t *qB,
+                          const uint8_t *sA, const uint8_t *sB,
+                          uint16_t *C, double *C64)
+{
+    const int64_t KB = (K + 31) / 32, KH = (K + 1) / 2;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = oracle_e2m1_to_f64(fp4_at(qA + m * KH, k)) *
+                           oracle_e8m0_to_f64(sA[m * KB + k / 32]);
+                double b = oracle_e2m1_to_f64(fp4_at(qB + n * KH, k)) *
+                           oracle_e8m0_to_f64(sB[n * KB + k / 32]);
+                acc += a * b;
+            }
+            if (C64) C64[m * N + n] = acc;
+            if (C) C[m * N + n] = oracle_f64_to_bf16(acc);
+        }
+    }
+}
+
+/*
  * Sampled forms: the same sums, for a list of P output positions
  * (rows[p], cols[p]) only, so that full-size problems can be checked
  * one output at a time.  out[p] / out64[p] receive C[rows[p]][cols[p]].
@@ -400,6 +454,36 @@ void oracle_gemm_mxfp8_nt_at(int64_t M, int64_t N, int64_t K,
         if (out64) out64[p] = acc;
         if (out) out[p] = oracle_f64_to_bf16(acc);
     }
+}
+
+void oracle_gemm_mxfp4_nt_at(int64_t M, int64_t N, int64_t K,
+                             const uint8_t *qA, const uint8_t *qB,
+                             const uint8_t *sA, const uint8_t *sB,
+                             int64_t P, const int64_t *rows, const int64_t *cols,
+                             uint16_t *out, double *out64)
+{
+    (void)M; (void)N;
+    const int64_t KB = (K + 31) / 32, KH = (K + 1) / 2;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = rows[p], n = cols[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = oracle_e2m1_to_f64(fp4_at(qA + m * KH, k)) *
+                       oracle_e8m0_to_f64(sA[m * KB + k / 32]);
+            double b = oracle_e2m1_to_f64(fp4_at(qB + n * KH, k)) *
+                       oracle_e8m0_to_f64(sB[n * KB + k / 32]);
+            acc += a * b;
+        }
+        if (out64) out64[p] = acc;
+        if (out) out[p] = oracle_f64_to_bf16(acc);
+    }
+}
+
+/* Elementwise FP4 decoding, for the tests. */
+void oracle_decode_e2m1(int64_t n, const uint8_t *nibbles, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_to_f64(nibbles[i] & 15);
 }
 
 /* Number of OpenMP threads a parallel region of this library would use. */

@@ -24,6 +24,10 @@ import torch
 
 FP8_E4M3_MAX = 448.0
 SCALE_BLOCK_K = 128
+FP4_E2M1_MAX = 6.0
+FP4_BLOCK_K = 32                     # OCP MX block: one scale per 32 elements
+# Magnitudes of the FP4 E2M1 codes 0..7 (sign in bit 3).
+FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
 @dataclasses.dataclass(frozen=True)
@@ -54,6 +58,8 @@ WORKLOADS = {
         Workload("mxfp8_nt_4096", "mxfp8_nt", 4096, 4096, 4096,
                  "block-scaled fp8 (e4m3 + e8m0 per 128 K) NT GEMM M=N=K=4096"),
         # The step before the block-scaled GEMM: one of its operands, quantised.
+        Workload("mxfp4_nt_4096", "mxfp4_nt", 4096, 4096, 4096,
+                 "block-scaled fp4 (e2m1 + e8m0 per 32 K) NT GEMM M=N=K=4096"),
         Workload("quant_mxfp8_4096", "quant_mxfp8", 4096, 0, 4096,
                  "block-scale quantiser fp32 -> e4m3fn + e8m0 per 128 K, M=K=4096"),
     )
@@ -107,6 +113,37 @@ def quantize_mxfp8(x: torch.Tensor):
     return q.contiguous().view(torch.uint8).numpy().copy(), scales
 
 
+def pack_fp4(codes: np.ndarray) -> np.ndarray:
+    """FP4 codes (R, K), K even -> bytes (R, K/2): element 2i in the low nibble."""
+    c = codes.astype(np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def quantize_mxfp4(x: torch.Tensor):
+    """Quantise float32 rows (R, K), K % 32 == 0, to packed E2M1 with one e8m0
+    scale per 32 K elements: the smallest 2^e with absmax <= 6 * 2^e (the
+    same rule as the fp8 inputs, with FP4's largest value), then each
+    x * 2^-e rounded to the nearest E2M1 value, ties to the even code.
+    Returns (q uint8 (R, K/2), scales uint8 (R, K/32))."""
+    xr = x.double().numpy()
+    R, K = xr.shape
+    KB = K // FP4_BLOCK_K
+    blocks = xr.reshape(R, KB, FP4_BLOCK_K)
+    absmax = np.abs(blocks).max(axis=2)
+    frac, exp = np.frexp(absmax)             # absmax = frac * 2^exp, frac in [0.5, 1)
+    # absmax / 2^(exp-3) = 8 frac in [4, 8): <= 6 iff frac <= 0.75.
+    e = exp.astype(np.int64) - 3 + (frac > FP4_E2M1_MAX / 8.0)
+    e = np.clip(np.where(absmax == 0.0, -127, e), -127, 127)
+    y = blocks * np.exp2(-e)[:, :, None]                      # exact power-of-two scaling
+    a = np.abs(y).reshape(R, K)
+    lo = np.clip(np.searchsorted(FP4_GRID, a, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    dlo, dhi = a - FP4_GRID[lo], FP4_GRID[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo) | (np.signbit(y.reshape(R, K)) & (a > 0)).astype(np.int64) << 3
+    return pack_fp4(code), (e + 127).astype(np.uint8)
+
+
 def make_inputs(w: Workload | str, seed: int = 0):
     """Inputs of a workload as a dict of numpy bit-pattern arrays.
 
@@ -128,6 +165,12 @@ def make_random(kind: str, M: int, N: int, K: int, seed: int = 0):
                 "B": randn_bits((K, N), torch.float16, g)}
     if kind == "quant_mxfp8":
         return {"X": randn_f32((M, K), g).numpy()}
+    if kind == "mxfp4_nt":
+        a = randn_f32((M, K), g)
+        b = randn_f32((N, K), g)
+        qA, sA = quantize_mxfp4(a)
+        qB, sB = quantize_mxfp4(b)
+        return {"qA": qA, "qB": qB, "sA": sA, "sB": sB}
     if kind == "mxfp8_nt":
         a = randn_f32((M, K), g)
         b = randn_f32((N, K), g)
@@ -153,6 +196,14 @@ def make_integer(kind: str, M: int, N: int, K: int, seed: int = 0, lo: int = -2,
         return {"A": to_bits(ints((M, K)).bfloat16()), "B": to_bits(ints((N, K)).bfloat16())}
     if kind == "f16_nn":
         return {"A": to_bits(ints((M, K)).half()), "B": to_bits(ints((K, N)).half())}
+    if kind == "mxfp4_nt":
+        # Integers in [lo, hi] are E2M1 codes 0 (0), 2 (1), 4 (2) with sign bit 8.
+        code = {0: 0, 1: 2, 2: 4, -1: 10, -2: 12}
+        lut = np.array([code[v] for v in range(-2, 3)], np.uint8)
+        KB = K // FP4_BLOCK_K
+        qA = pack_fp4(lut[ints((M, K)).numpy().astype(np.int64) + 2])
+        qB = pack_fp4(lut[ints((N, K)).numpy().astype(np.int64) + 2])
+        return {"qA": qA, "qB": qB, "sA": np.full((M, KB), 127, np.uint8), "sB": np.full((N, KB), 127, np.uint8)}
     if kind == "mxfp8_nt":
         KB = (K + SCALE_BLOCK_K - 1) // SCALE_BLOCK_K
         qA = ints((M, K)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
