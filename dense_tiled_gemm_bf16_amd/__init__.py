@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_bf16_nt.argtypes = [i64, i64, i64, p, p, p, p]
     L.gemm_f16_nn.argtypes = [i64, i64, i64, p, p, p, p]
     L.gemm_mxfp8_nt.argtypes = [i64, i64, i64, p, p, p, p, p, p]
+    L.gemm_mxfp4_nt.argtypes = [i64, i64, i64, p, p, p, p, p, p]
+    L.gemm_mxfp4_nt.restype = ctypes.c_int
     for f in (L.gemm_bf16_nt, L.gemm_f16_nn, L.gemm_mxfp8_nt):
         f.restype = ctypes.c_int
     L.tgemm_init.argtypes = []
@@ -213,3 +215,23 @@ def gemm(a, b, out=None, stream=None):
     fn = lib().gemm_bf16 if a.dtype == torch.bfloat16 else lib().gemm_f16
     check(fn(ta, tb, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, _stream_ptr(stream)))
     return out
+
+
+def gemm_mxfp4_nt(a, b, scale_a, scale_b, out=None, stream=None):
+    """Block-scaled FP4 NT GEMM -> bf16 (M,N).
+
+    a (M,K/2), b (N,K/2): packed E2M1 bytes (uint8; element 2i in the low
+    nibble of byte i); scale_a (M,K/32), scale_b (N,K/32): e8m0 bytes.
+    """
+    torch = _torch()
+    M, KH = a.shape
+    N = b.shape[0]
+    K = 2 * KH
+    _want(a, "a", torch.uint8, (M, KH))
+    _want(b, "b", torch.uint8, (N, KH))
+    _want(scale_a, "scale_a", torch.uint8, (M, K // 32))
+    _want(scale_b, "scale_b", torch.uint8, (N, K // 32))
+    c = _out(out, (M, N), torch.bfloat16, a)
+    check(lib().gemm_mxfp4_nt(M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
+                              scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    return c

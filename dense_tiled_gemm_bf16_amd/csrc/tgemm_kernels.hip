@@ -89,13 +89,15 @@ struct Args {
 
 // Element type of A and B, and the storage of each: AK, A is M x K
 // (K-contiguous; else K x M); BK, B is N x K (K-contiguous; else K x N).
-enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2 };
+// fp4 operands are handled as rows of bytes (two E2M1 elements each):
+// kElem = 1 and K counts bytes inside the kernel.
+enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2, kFp4 = 3 };
 template <int DT, bool AK, bool BK>
 struct Traits {
   static constexpr int kDt = DT;
-  static constexpr int kElem = DT == kFp8 ? 1 : 2;
+  static constexpr int kElem = DT == kFp8 || DT == kFp4 ? 1 : 2;
   static constexpr bool kAK = AK, kBK = BK;
-  static constexpr bool kScaled = DT == kFp8;
+  static constexpr bool kScaled = DT == kFp8 || DT == kFp4;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -261,7 +263,9 @@ struct Kernel {
   static constexpr int kNBm = kWM / kBlk;       // blocks per wave along M (y blocks)
   static constexpr int kNBn = kWN / kBlk;       // blocks per wave along N (x blocks)
   static constexpr int kNR = kNBm + kNBn;       // fragment reads per substep
-  static constexpr int kPerSub = kNBm * kNBn;   // MFMAs per substep
+  // fp4: a 32-byte fragment holds 64 K elements, two MFMAs of 32 per lane.
+  static constexpr int kHalves = T::kDt == kFp4 ? 2 : 1;
+  static constexpr int kPerSub = kNBm * kNBn * kHalves;  // MFMAs per substep
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
   static constexpr int kLA = TM / 32, kLB = TN / 32;  // load instructions per wave per slice
   static constexpr int kLoads = kLA + kLB;
@@ -347,6 +351,14 @@ struct Kernel {
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside that dword pair
   uint32_t sc_raw[4][2];          // the next group, in flight
   int sc_nxt[8], sc_cur[8];       // per block (4 x blocks, then 4 y blocks): bytes of 4 slices
+  // fp4: one scale per 32 elements, so a slice (256 elements) has 8 per
+  // row, consecutive in memory.  Each lane loads the three aligned dwords
+  // holding its row's 8 for one slice (instruction j as above), shifts them
+  // into two dwords (groups 0-3, 4-7) and keeps, for the lanes feeding that
+  // row, the bytes each half of the wave needs: the MFMA of substep s, half
+  // h of a lane in wave half w uses group 4 s + 2 w + h, so lanes 0-31 take
+  // groups 0, 1, 4, 5 and lanes 32-63 groups 2, 3, 6, 7, in byte 2 s + h.
+  uint32_t sc4_raw[4][3];
   Acc acc[kNBn][kNBm];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
@@ -401,7 +413,8 @@ struct Kernel {
 
   // FIRST: the first K substep, whose MFMAs start from an accumulator of 0
   // (an inline constant), so the accumulators are never written by VALU code.
-  template <bool FIRST, int JB = 0>
+  // SEL: byte of the scale registers to use; H: half of an fp4 fragment.
+  template <bool FIRST, int SEL = 0, int H = 0>
   __device__ static __forceinline__ Acc mma(const Frag &x, const Frag &y, const Acc &c, int sx, int sy) {
     // The 16 x 16 forms are written as inline asm with the accumulator tied
     // in place ("+a"): with the builtin the register allocator rotates the
@@ -423,10 +436,17 @@ struct Kernel {
       else
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
       return d;
-    } else {
-      // Format code 0 (OCP FP8 E4M3) for both operands; byte JB of each
+    } else if constexpr (T::kDt == kFp8) {
+      // Format code 0 (OCP FP8 E4M3) for both operands; byte SEL of each
       // scale VGPR (the slice's place in its group of 4).
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, JB, sx, JB, sy);
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, SEL, sx, SEL, sy);
+    } else {
+      // Format code 4 (OCP FP4 E2M1): 16 bytes, 32 elements per lane, taken
+      // from half H of the fragment (the compiler reads the 4 registers in
+      // place); byte SEL of each scale VGPR.
+      const i32x8 xh = {x[4 * H], x[4 * H + 1], x[4 * H + 2], x[4 * H + 3], 0, 0, 0, 0};
+      const i32x8 yh = {y[4 * H], y[4 * H + 1], y[4 * H + 2], y[4 * H + 3], 0, 0, 0, 0};
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xh, yh, c, 4, 4, SEL, sx, SEL, sy);
     }
   }
 
@@ -499,6 +519,34 @@ struct Kernel {
     }
   }
 
+  // fp4: scale bytes of slice s (8 per row); a slice past the last scale
+  // block loads nothing.
+  __device__ __forceinline__ void load_scales4(int s) {
+    const bool ok = 8 * s < a.kb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+        sc4_raw[j][d] = __builtin_amdgcn_raw_buffer_load_b32(rss[j >> 1], ok ? sc_off[j] + 4 * d : kOOB, 8u * s, 0);
+  }
+
+  __device__ __forceinline__ void convert_scales4() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d0 = __builtin_amdgcn_alignbyte(sc4_raw[j][1], sc4_raw[j][0], sc_sh[j]);
+      const uint32_t d1 = __builtin_amdgcn_alignbyte(sc4_raw[j][2], sc4_raw[j][1], sc_sh[j]);
+      const int lo = (int)__builtin_amdgcn_perm(d1, d0, 0x05040100u);  // groups 0, 1, 4, 5
+      const int hi = (int)__builtin_amdgcn_perm(d1, d0, 0x07060302u);  // groups 2, 3, 6, 7
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int src = (32 * h + (lane & 31)) << 2;
+        const int vlo = __builtin_amdgcn_ds_bpermute(src, lo);
+        const int vhi = __builtin_amdgcn_ds_bpermute(src, hi);
+        sc_nxt[2 * j + h] = lane < 32 ? vlo : vhi;
+      }
+    }
+  }
+
   // The loaded group, shifted and redistributed: block 2 j + h of
   // instruction j's rows is rows 32 h .. 32 h + 31, which lane l (both
   // halves of the wave) takes from lane 32 h + l % 32.
@@ -522,7 +570,7 @@ struct Kernel {
   template <int S, int JB, bool FIRST, int Q>
   __device__ __forceinline__ void mfma_one(int kt, Frags &f0, Frags &f1) {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
-    constexpr int I = q / kNBm, J = q % kNBm;
+    constexpr int H = q % kHalves, I = q / kHalves / kNBm, J = q / kHalves % kNBm;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
     if constexpr (Q == kBarrierAt) {
       // The prefetch issued after the last needed load may be outstanding
@@ -531,7 +579,13 @@ struct Kernel {
       wait_vm_lgkm0<kPfOut>();
       barrier();
       // Scales of the next group: waited for by the next slice's barrier.
-      if constexpr (T::kScaled && JB == 1) load_scale_group((kt + 3) >> 2);
+      if constexpr (T::kDt == kFp8 && JB == 1) load_scale_group((kt + 3) >> 2);
+      // fp4: the scales of slice kt + 1 (loaded at the last barrier) into
+      // the next set, then those of slice kt + 2.
+      if constexpr (T::kDt == kFp4) {
+        convert_scales4();
+        load_scales4(kt + 2);
+      }
     }
     if constexpr (Q < kNR) read_one<S, Q>(f1, 1);
     if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNR) read_one<S ^ 1, Q - kBarrierAt>(f0, 0);
@@ -539,7 +593,10 @@ struct Kernel {
     if constexpr (kTail >= 0) load_one<S>(kt + 2, kTail);
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
     const Frags &f = SUB == 0 ? f0 : f1;
-    if constexpr (T::kScaled)
+    if constexpr (T::kDt == kFp4)
+      acc[I][J] = mma<FIRST && SUB == 0 && H == 0, 2 * SUB + H, H>(f.x[I], f.y[J], acc[I][J], sc_cur[I],
+                                                                   sc_cur[4 + J]);
+    else if constexpr (T::kScaled)
       acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
       acc[I][J] = mma<FIRST && SUB == 0>(f.x[I], f.y[J], acc[I][J], 0, 0);
@@ -555,8 +612,8 @@ struct Kernel {
   // = kt % 4 for the block-scaled kind.
   template <int S, int JB, bool FIRST = false>
   __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
-    if constexpr (T::kScaled && JB == 3) convert_scales();  // the group loaded in slice kt - 2
-    if constexpr (T::kScaled && JB == 0 && !FIRST) {
+    if constexpr (T::kDt == kFp8 && JB == 3) convert_scales();  // the group loaded in slice kt - 2
+    if constexpr ((T::kDt == kFp8 && JB == 0 && !FIRST) || (T::kDt == kFp4 && !FIRST)) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
     }
@@ -623,17 +680,26 @@ struct Kernel {
         for (int j = 0; j < kNBm; ++j) acc[i][j] = Acc{};
     }
 
-    // Prologue: the scales of slices 0-3, slice 0 into slot 0, the loads
-    // of slice 1 that a previous slice's tail would have issued; wait for
-    // the first two.  (With K = 0 every slice is all zeros.)
-    if constexpr (T::kScaled) load_scale_group(0);
+    // Prologue: the scales of slices 0-3 (fp4: of slice 0, converted at
+    // once, then of slice 1), slice 0 into slot 0, the loads of slice 1 that
+    // a previous slice's tail would have issued; wait for the first two.
+    // (With K = 0 every slice is all zeros.)
+    if constexpr (T::kDt == kFp8) load_scale_group(0);
+    if constexpr (T::kDt == kFp4) {
+      load_scales4(0);
+      wait_vm_lgkm0<0>();
+      convert_scales4();
+#pragma unroll
+      for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
+      load_scales4(1);
+    }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) load_one<0>(0, i);
     constexpr int kTailLoads = tail_loads();
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) load_one<1>(1, i);
     wait_vm_lgkm0<kTailLoads>();
-    if constexpr (T::kScaled) {
+    if constexpr (T::kDt == kFp8) {
       convert_scales();
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
@@ -646,7 +712,7 @@ struct Kernel {
     // arrives as zeros and adds nothing.  (Leaving the loop early instead
     // makes the register allocator copy the accumulators around and spill.)
     step<0, 0, true>(0, f0, f1);
-    if constexpr (T::kScaled) {
+    if constexpr (T::kDt == kFp8) {
       for (int kt = 1; kt < nk; kt += 4) {
         step<1, 1>(kt, f0, f1);
         step<0, 2>(kt + 1, f0, f1);
@@ -816,9 +882,15 @@ hipError_t launch(const Problem &p) {
   const int slice = p.dt == Dt::kMxfp8 ? 128 : 64;
   a.ksteps = (int)((p.K + slice - 1) / slice);
   a.kb = (int)((p.K + 127) / 128);
+  if (p.dt == Dt::kMxfp4) {
+    // Rows of bytes (two elements each), 128-byte slices, a scale per 32.
+    a.K = (int)(p.K / 2);
+    a.ksteps = (a.K + kRowBytes - 1) / kRowBytes;
+    a.kb = (int)((p.K + 31) / 32);
+  }
   int tm = p.tile_m, tn = p.tile_n;
   if (tm == 0) {
-    const Shape s = p.dt == Dt::kMxfp8 ? Shape{256, 256, 1.0}
+    const Shape s = p.dt == Dt::kMxfp8 || p.dt == Dt::kMxfp4 ? Shape{256, 256, 1.0}
                     : p.trans_b        ? pick_shape(kShapesBK, p.M, p.N, p.cus)
                                        : pick_shape(kShapesBN, p.M, p.N, p.cus);
     tm = s.tm;
@@ -833,12 +905,16 @@ hipError_t launch(const Problem &p) {
       if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
         return launch_shape<Traits<kFp8, true, true>, 256, 256>(p, a);
       break;
+    case Dt::kMxfp4:
+      if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
+        return launch_shape<Traits<kFp4, true, true>, 256, 256>(p, a);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
 bool shape_supported(const Problem &p, int tile_m, int tile_n) {
-  if (p.dt == Dt::kMxfp8) return tile_m == 256 && tile_n == 256;
+  if (p.dt == Dt::kMxfp8 || p.dt == Dt::kMxfp4) return tile_m == 256 && tile_n == 256;
   return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128) ||
          (tile_m == 256 && tile_n == 192 && p.trans_b);
 }

@@ -116,6 +116,34 @@ TGEMM_API int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K,
                   void *C, hipStream_t stream);
 
 /*
+ * Block-scaled FP4 ("MXFP4") C = (sA * A) . (sB * B)^T, bf16 out.
+ *
+ * The Blackwell TCGEN05 GEMM tutorial, section "进阶" (Advanced), names
+ * MXFP8 "and other" block-scaled formats.  The pages fix no layout for
+ * them; this follows the OCP MX format: OCP FP4 E2M1 elements (values 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6 with a sign bit) packed two per byte, element 2i
+ * in the low nibble of byte i, and one OCP E8M0 scale per 32 consecutive
+ * K elements.
+ *
+ *   A        device pointer, M x K/2 bytes, row-major (row m holds A[m][0..K-1])
+ *   B        device pointer, N x K/2 bytes, row-major
+ *   scale_A  device pointer, M x K/32 e8m0 bytes: scale_A[m][j] scales
+ *            A[m][32 j .. 32 j + 31]
+ *   scale_B  device pointer, N x K/32 e8m0 bytes
+ *   C        device pointer, M x N bf16, row-major; written, never read
+ *
+ * C[m][n] is the fp32 sum over k of
+ *   A[m][k] * 2^(scale_A[m][k/32] - 127) * B[n][k] * 2^(scale_B[n][k/32] - 127),
+ * rounded to nearest-even bf16.  K == 0 writes zeros.
+ * Requirements: K % 32 == 0, N % 8 == 0, A, B and C 16-byte aligned (the
+ * scale arrays need no alignment), 256 * K / 2 < 2^31.
+ */
+TGEMM_API int gemm_mxfp4_nt(int64_t M, int64_t N, int64_t K,
+                  const void *A, const void *B,
+                  const void *scale_A, const void *scale_B,
+                  void *C, hipStream_t stream);
+
+/*
  * C = op(A) . op(B) for 16-bit inputs with any operand storage and row
  * strides: bfloat16 in and out (gemm_bf16), fp16 in and out (gemm_f16);
  * fp32 accumulation.
@@ -196,7 +224,7 @@ TGEMM_API const char *tgemm_last_error(void);
  * block_M / block_N; velog "tilelang", 1.1 Front-End DSL).
  *   B stored N x K (gemm_bf16_nt, trans_b = 1): 256x256, 256x192, 128x128
  *   B stored K x N (gemm_f16_nn, trans_b = 0):  256x256, 128x128
- *   gemm_mxfp8_nt: 256x256
+ *   gemm_mxfp8_nt, gemm_mxfp4_nt: 256x256
  * Returns TGEMM_OK, or TGEMM_EINVAL for a shape no entry point has; an
  * entry point called with a shape it does not have returns TGEMM_EINVAL.
  * The result does not depend on the tile shape beyond the order of the

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
+        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_mxfp4_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
          "tgemm_last_error", "tgemm_set_tile"])
 
 
