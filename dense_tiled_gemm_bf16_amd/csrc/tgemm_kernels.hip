@@ -339,26 +339,31 @@ struct Kernel {
   typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type lb;
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
-  // Block scales (fp8).  They are fetched once per group of 4 slices: a
-  // row's scale bytes for slices 4 g .. 4 g + 3 are consecutive, so each
-  // lane loads the two aligned dwords that hold them for one of 64 rows
-  // (instruction j: the wave's B rows 64 j .. + 63 for j < 2, its A rows
-  // 64 (j - 2) .. + 63 after), shifts them into one dword and hands it to
-  // the lanes that feed that row to the MFMA.  The MFMA's byte select then
-  // picks the slice, so no per-slice work remains.
+  // Block scales.  Each lane streams the scale bytes of one row per
+  // "instruction" j (the wave's B rows 64 j .. + 63 for j < 2, its A rows
+  // 64 (j - 2) .. + 63 after) in 16-byte chunks: chunk c is the 16 bytes
+  // from the dword holding the row's first scale byte, plus 16 c.  Any 4
+  // consecutive bytes of the row that start in chunk c can be shifted out
+  // of it and the next chunk's first dword, so two chunks are kept.  A
+  // chunk covers 16 slices of fp8 (one scale per 128 K) or 2 of fp4 (8 per
+  // 256-element slice).  Loading a row's bytes 16 at a time keeps the
+  // texture unit's work small: each of these loads touches 64 cache lines
+  // (one per lane), as many as a 1 KB panel load touches bytes / 16.
+  //  * fp8: group g (slices 4 g .. 4 g + 3) is one shifted dword, handed
+  //    to the lanes that feed that row to the MFMA; the MFMA's byte select
+  //    then picks the slice.
+  //  * fp4: slice t is two shifted dwords (groups 0-3, 4-7); the MFMA of
+  //    substep s, half h of a lane in wave half w uses group 4 s + 2 w + h,
+  //    so lanes 0-31 take groups 0, 1, 4, 5 and lanes 32-63 groups 2, 3, 6,
+  //    7, in byte 2 s + h.
+  // Bytes past the row's last scale block (the next row's, in a padded
+  // slice) are zeroed: the slices they would scale hold zeros, and a NaN
+  // scale (0xff) would turn those zeros into NaN.
   __amdgpu_buffer_rsrc_t rss[2];  // B scales, A scales; based at the tile's first row, dword aligned
   uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
-  uint32_t sc_sh[4];              // per instruction: byte shift of the row inside that dword pair
-  uint32_t sc_raw[4][2];          // the next group, in flight
-  int sc_nxt[8], sc_cur[8];       // per block (4 x blocks, then 4 y blocks): bytes of 4 slices
-  // fp4: one scale per 32 elements, so a slice (256 elements) has 8 per
-  // row, consecutive in memory.  Each lane loads the three aligned dwords
-  // holding its row's 8 for one slice (instruction j as above), shifts them
-  // into two dwords (groups 0-3, 4-7) and keeps, for the lanes feeding that
-  // row, the bytes each half of the wave needs: the MFMA of substep s, half
-  // h of a lane in wave half w uses group 4 s + 2 w + h, so lanes 0-31 take
-  // groups 0, 1, 4, 5 and lanes 32-63 groups 2, 3, 6, 7, in byte 2 s + h.
-  uint32_t sc4_raw[4][3];
+  uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
+  u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction
+  int sc_nxt[8], sc_cur[8];       // per block (4 x blocks, then 4 y blocks): bytes of 4 slices / groups
   Acc acc[kNBn][kNBm];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
@@ -508,33 +513,33 @@ struct Kernel {
                                              ok ? pf_off : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
   }
 
-  // Scale dwords of group g (slices 4 g .. 4 g + 3); a group past the last
-  // scale block loads nothing (its slices are all zeros).
-  __device__ __forceinline__ void load_scale_group(int g) {
-    const bool ok = 4 * g < a.kb;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc_raw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rss[j >> 1], ok ? sc_off[j] : kOOB, 4u * g, 0);
-      sc_raw[j][1] = __builtin_amdgcn_raw_buffer_load_b32(rss[j >> 1], ok ? sc_off[j] + 4 : kOOB, 4u * g, 0);
-    }
-  }
-
-  // fp4: scale bytes of slice s (8 per row); a slice past the last scale
-  // block loads nothing.
-  __device__ __forceinline__ void load_scales4(int s) {
-    const bool ok = 8 * s < a.kb;
+  // Chunk c of every instruction's row into dst.  The resource ends at the
+  // dword holding the tile's last scale byte; the hardware checks each dword
+  // of the load against it (soffset included), so dwords past it read 0.
+  __device__ __forceinline__ void load_chunks(u32x4 (&dst)[4], int c) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int d = 0; d < 3; ++d)
-        sc4_raw[j][d] = __builtin_amdgcn_raw_buffer_load_b32(rss[j >> 1], ok ? sc_off[j] + 4 * d : kOOB, 8u * s, 0);
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rss[j >> 1], sc_off[j], 16u * (uint32_t)c, 0);
   }
 
-  __device__ __forceinline__ void convert_scales4() {
+  // Mask keeping the bytes of a dword that holds scale blocks b .. b + 3 of
+  // a row with kb blocks (nv = kb - b of them valid).
+  __device__ static __forceinline__ uint32_t keep_mask(int nv) {
+    return nv >= 4 ? ~0u : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+  }
+
+  // fp4: slice t's 8 scale bytes per row, from chunk t / 2 (ODD: t odd, its
+  // second half, plus the next chunk's first dword), into sc_nxt.
+  template <bool ODD>
+  __device__ __forceinline__ void convert_scales4(int t) {
+    const uint32_t keep0 = keep_mask(a.kb - 8 * t), keep1 = keep_mask(a.kb - 8 * t - 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t d0 = __builtin_amdgcn_alignbyte(sc4_raw[j][1], sc4_raw[j][0], sc_sh[j]);
-      const uint32_t d1 = __builtin_amdgcn_alignbyte(sc4_raw[j][2], sc4_raw[j][1], sc_sh[j]);
+      const uint32_t w0 = ODD ? sc_ck[j][2] : sc_ck[j][0];
+      const uint32_t w1 = ODD ? sc_ck[j][3] : sc_ck[j][1];
+      const uint32_t w2 = ODD ? sc_ckn[j][0] : sc_ck[j][2];
+      const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sc_sh[j]) & keep0;
+      const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sc_sh[j]) & keep1;
       const int lo = (int)__builtin_amdgcn_perm(d1, d0, 0x05040100u);  // groups 0, 1, 4, 5
       const int hi = (int)__builtin_amdgcn_perm(d1, d0, 0x07060302u);  // groups 2, 3, 6, 7
 #pragma unroll
@@ -547,16 +552,24 @@ struct Kernel {
     }
   }
 
-  // The loaded group, shifted and redistributed: block 2 j + h of
-  // instruction j's rows is rows 32 h .. 32 h + 31, which lane l (both
-  // halves of the wave) takes from lane 32 h + l % 32.
-  __device__ __forceinline__ void convert_scales() {
+  // fp8: group g, shifted out of the window's first two dwords and
+  // redistributed into sc_nxt: block 2 j + h of instruction j's rows is
+  // rows 32 h .. 32 h + 31, which lane l (both halves of the wave) takes
+  // from lane 32 h + l % 32.  The window (chunk, next chunk) then moves on
+  // by one dword; once it has moved a whole chunk the chunk after the next
+  // is loaded, 16 slices ahead of its first use.  (Moving the window keeps
+  // every register index static.)
+  __device__ __forceinline__ void convert_scales(int g) {
+    const uint32_t keep = keep_mask(a.kb - 4 * g);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int d = (int)__builtin_amdgcn_alignbyte(sc_raw[j][1], sc_raw[j][0], sc_sh[j]);
+      const int d = (int)(__builtin_amdgcn_alignbyte(sc_ck[j][1], sc_ck[j][0], sc_sh[j]) & keep);
       sc_nxt[2 * j] = __builtin_amdgcn_ds_bpermute((lane & 31) << 2, d);
       sc_nxt[2 * j + 1] = __builtin_amdgcn_ds_bpermute((32 + (lane & 31)) << 2, d);
+      sc_ck[j] = u32x4{sc_ck[j][1], sc_ck[j][2], sc_ck[j][3], sc_ckn[j][0]};
+      sc_ckn[j] = u32x4{sc_ckn[j][1], sc_ckn[j][2], sc_ckn[j][3], 0u};
     }
+    if ((g & 3) == 3) load_chunks(sc_ckn, (g >> 2) + 2);
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
@@ -578,13 +591,17 @@ struct Kernel {
       constexpr int kPfOut = kPfDist > 0 && (kPfHead || !FIRST) ? 1 : 0;
       wait_vm_lgkm0<kPfOut>();
       barrier();
-      // Scales of the next group: waited for by the next slice's barrier.
-      if constexpr (T::kDt == kFp8 && JB == 1) load_scale_group((kt + 3) >> 2);
-      // fp4: the scales of slice kt + 1 (loaded at the last barrier) into
-      // the next set, then those of slice kt + 2.
+      // fp4: the scales of slice kt + 1 into the next set.  An odd slice
+      // ends chunk (kt + 1) / 2: the next chunk moves up and the one after
+      // it is loaded (waited for by the next barrier, used after the one
+      // after).
       if constexpr (T::kDt == kFp4) {
-        convert_scales4();
-        load_scales4(kt + 2);
+        convert_scales4<(JB & 1) == 0>(kt + 1);
+        if constexpr ((JB & 1) == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc_ck[j] = sc_ckn[j];
+          load_chunks(sc_ckn, (kt >> 1) + 2);
+        }
       }
     }
     if constexpr (Q < kNR) read_one<S, Q>(f1, 1);
@@ -612,7 +629,7 @@ struct Kernel {
   // = kt % 4 for the block-scaled kind.
   template <int S, int JB, bool FIRST = false>
   __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
-    if constexpr (T::kDt == kFp8 && JB == 3) convert_scales();  // the group loaded in slice kt - 2
+    if constexpr (T::kDt == kFp8 && JB == 3) convert_scales((kt + 1) >> 2);
     if constexpr ((T::kDt == kFp8 && JB == 0 && !FIRST) || (T::kDt == kFp4 && !FIRST)) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
@@ -680,18 +697,13 @@ struct Kernel {
         for (int j = 0; j < kNBm; ++j) acc[i][j] = Acc{};
     }
 
-    // Prologue: the scales of slices 0-3 (fp4: of slice 0, converted at
-    // once, then of slice 1), slice 0 into slot 0, the loads of slice 1 that
-    // a previous slice's tail would have issued; wait for the first two.
-    // (With K = 0 every slice is all zeros.)
-    if constexpr (T::kDt == kFp8) load_scale_group(0);
-    if constexpr (T::kDt == kFp4) {
-      load_scales4(0);
-      wait_vm_lgkm0<0>();
-      convert_scales4();
-#pragma unroll
-      for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
-      load_scales4(1);
+    // Prologue: the first two scale chunks, slice 0 into slot 0, the loads
+    // of slice 1 that a previous slice's tail would have issued; wait for
+    // all but those, and convert slice 0's scales.  (With K = 0 every slice
+    // is all zeros.)
+    if constexpr (T::kScaled) {
+      load_chunks(sc_ck, 0);
+      load_chunks(sc_ckn, 1);
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) load_one<0>(0, i);
@@ -699,8 +711,11 @@ struct Kernel {
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) load_one<1>(1, i);
     wait_vm_lgkm0<kTailLoads>();
-    if constexpr (T::kDt == kFp8) {
-      convert_scales();
+    if constexpr (T::kScaled) {
+      if constexpr (T::kDt == kFp8)
+        convert_scales(0);
+      else
+        convert_scales4<false>(0);
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
     }

@@ -223,6 +223,42 @@ def test_mxfp8_unaligned_scale_pointers(offset):
     assert_bitwise(to_bits(c), oracle_full("mxfp8_nt", x), f"mxfp8 scales at offset {offset}")
 
 
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_mxfp8_unaligned_scales_long_K(offset):
+    """37 scale blocks per row (K = 4736): the kernel streams each row's
+    scale bytes in 16-byte pieces, so a row whose bytes start at any byte of
+    a dword is read across several of them.  Bitwise on integer elements."""
+    M, N, K = 264, 136, 4736
+    x = workloads.make_integer("mxfp8_nt", M, N, K, seed=40 + offset)
+    rng = np.random.default_rng(40 + offset)
+    x["sA"] = rng.integers(124, 131, x["sA"].shape).astype(np.uint8)
+    x["sB"] = rng.integers(124, 131, x["sB"].shape).astype(np.uint8)
+
+    def at_offset(bits):
+        buf = torch.zeros(bits.size + offset, dtype=torch.uint8, device="cuda")
+        buf[offset:] = torch.from_numpy(np.ascontiguousarray(bits).reshape(-1)).cuda()
+        return buf[offset:].view(bits.shape)
+
+    print(f"[gpu] mxfp8_nt long-K unaligned scales offset={offset} M={M} N={N} K={K}", flush=True)
+    c = tg.gemm_mxfp8_nt(to_dev(x["qA"], ""), to_dev(x["qB"], ""), at_offset(x["sA"]), at_offset(x["sB"]))
+    torch.cuda.synchronize()
+    assert_bitwise(to_bits(c), oracle_full("mxfp8_nt", x), f"mxfp8 long K scales at offset {offset}")
+
+
+def test_mxfp8_next_rows_scales_do_not_leak():
+    """K = 768: 6 slices of 128, run as 8 (the last two all zeros), whose
+    scale bytes would be the next row's.  Odd rows of A and B get 0xff
+    scales (NaN in the e8m0 format); the products of even rows and even
+    columns use none of them and must equal the oracle bit for bit."""
+    M, N, K = 64, 64, 768
+    x = workloads.make_integer("mxfp8_nt", M, N, K, seed=31)
+    x["sA"][1::2] = 0xFF
+    x["sB"][1::2] = 0xFF
+    got = to_bits(run("mxfp8_nt", x, M, N, K))
+    ref = oracle_full("mxfp8_nt", x)
+    assert_bitwise(got[::2, ::2], ref[::2, ::2], "mxfp8 even rows and columns")
+
+
 @pytest.mark.parametrize("kind", ["bf16_nt", "f16_nn", "mxfp8_nt"])
 def test_mid_size_full_parity_several_tiles(kind):
     M, N, K = 776, 520, 1040 if kind != "mxfp8_nt" else 1024

@@ -85,6 +85,41 @@ def test_unaligned_scale_pointers(offset):
                    f"mxfp4 scales at offset {offset}")
 
 
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_unaligned_scales_long_K(offset):
+    """75 scale blocks per row (K = 2400), rows starting at every byte of a
+    dword: each row's scale bytes are streamed 16 at a time across several
+    such pieces.  Bitwise on integer elements."""
+    M, N, K = 264, 136, 2400
+    x = workloads.make_integer("mxfp4_nt", M, N, K, seed=50 + offset)
+    rng = np.random.default_rng(50 + offset)
+    x["sA"] = rng.integers(125, 130, x["sA"].shape).astype(np.uint8)
+    x["sB"] = rng.integers(125, 130, x["sB"].shape).astype(np.uint8)
+
+    def at_offset(bits):
+        buf = torch.zeros(bits.size + offset, dtype=torch.uint8, device="cuda")
+        buf[offset:] = torch.from_numpy(np.ascontiguousarray(bits).reshape(-1)).cuda()
+        return buf[offset:].view(bits.shape)
+
+    assert_bitwise(run(x, M, N, K, at_offset(x["sA"]), at_offset(x["sB"])), oracle_full(x),
+                   f"mxfp4 long K scales at offset {offset}")
+
+
+@pytest.mark.parametrize("K", [96, 1312])
+def test_next_rows_scales_do_not_leak(K):
+    """A slice is 8 scale blocks; with K = 96 (3 blocks) or 1312 (41) the
+    last slice's other blocks would be the next rows' bytes.  Odd rows of A
+    and B get 0xff scales (NaN in the e8m0 format); the products of even
+    rows and even columns use none of them and must equal the oracle."""
+    M, N = 64, 64
+    x = workloads.make_integer("mxfp4_nt", M, N, K, seed=K)
+    x["sA"][1::2] = 0xFF
+    x["sB"][1::2] = 0xFF
+    got = run(x, M, N, K)
+    ref = oracle_full(x)
+    assert_bitwise(got[::2, ::2], ref[::2, ::2], f"mxfp4 K={K} even rows and columns")
+
+
 def test_mid_size_full_parity():
     M, N, K = 776, 520, 1024
     x = workloads.make_random("mxfp4_nt", M, N, K, seed=11)
