@@ -540,22 +540,20 @@ struct Kernel {
       const uint32_t w2 = ODD ? sc_ckn[j][0] : sc_ck[j][2];
       const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sc_sh[j]) & keep0;
       const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sc_sh[j]) & keep1;
-      const int lo = (int)__builtin_amdgcn_perm(d1, d0, 0x05040100u);  // groups 0, 1, 4, 5
-      const int hi = (int)__builtin_amdgcn_perm(d1, d0, 0x07060302u);  // groups 2, 3, 6, 7
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int src = (32 * h + (lane & 31)) << 2;
-        const int vlo = __builtin_amdgcn_ds_bpermute(src, lo);
-        const int vhi = __builtin_amdgcn_ds_bpermute(src, hi);
-        sc_nxt[2 * j + h] = lane < 32 ? vlo : vhi;
-      }
+      const uint32_t lo = __builtin_amdgcn_perm(d1, d0, 0x05040100u);  // groups 0, 1, 4, 5
+      const uint32_t hi = __builtin_amdgcn_perm(d1, d0, 0x07060302u);  // groups 2, 3, 6, 7
+      // Block 2 j: lo of rows 0-31 in lanes 0-31, hi of the same rows in
+      // lanes 32-63; block 2 j + 1 likewise for rows 32-63.
+      const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+      sc_nxt[2 * j] = (int)sw[0];
+      sc_nxt[2 * j + 1] = (int)sw[1];
     }
   }
 
   // fp8: group g, shifted out of the window's first two dwords and
   // redistributed into sc_nxt: block 2 j + h of instruction j's rows is
   // rows 32 h .. 32 h + 31, which lane l (both halves of the wave) takes
-  // from lane 32 h + l % 32.  The window (chunk, next chunk) then moves on
+  // from lane 32 h + l % 32 (one swap of the wave halves).  The window (chunk, next chunk) then moves on
   // by one dword; once it has moved a whole chunk the chunk after the next
   // is loaded, 16 slices ahead of its first use.  (Moving the window keeps
   // every register index static.)
@@ -563,9 +561,10 @@ struct Kernel {
     const uint32_t keep = keep_mask(a.kb - 4 * g);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int d = (int)(__builtin_amdgcn_alignbyte(sc_ck[j][1], sc_ck[j][0], sc_sh[j]) & keep);
-      sc_nxt[2 * j] = __builtin_amdgcn_ds_bpermute((lane & 31) << 2, d);
-      sc_nxt[2 * j + 1] = __builtin_amdgcn_ds_bpermute((32 + (lane & 31)) << 2, d);
+      const uint32_t d = __builtin_amdgcn_alignbyte(sc_ck[j][1], sc_ck[j][0], sc_sh[j]) & keep;
+      const auto sw = __builtin_amdgcn_permlane32_swap(d, d, false, false);
+      sc_nxt[2 * j] = (int)sw[0];
+      sc_nxt[2 * j + 1] = (int)sw[1];
       sc_ck[j] = u32x4{sc_ck[j][1], sc_ck[j][2], sc_ck[j][3], sc_ckn[j][0]};
       sc_ckn[j] = u32x4{sc_ckn[j][1], sc_ckn[j][2], sc_ckn[j][3], 0u};
     }
