@@ -24,13 +24,14 @@
 //    offset and arrive as zeros (the pages' TMA zero OOB fill).
 //  * pipelined K loop: the pages use a 3-slot ring with producer and
 //    consumer warpgroups and mbarrier parity waits (velog "tilelang",
-//    Device IRModule).  Here every wave both loads and computes, with two
-//    slots: partway through slice kt's MFMAs (halfway for 16-bit inputs,
-//    three quarters for fp8) a wait and a barrier free slot kt % 2; the
-//    loads of slice kt + 2 into it then go out spread over the next half
-//    slice of MFMAs and have at least another half slice to land before
-//    they are needed.  The next slice's first operand reads follow the
-//    barrier, overlapping the current slice's remaining MFMAs.
+//    Device IRModule).  Here every wave both loads and computes, with a
+//    ring of NS slots (two for 256-row tiles, four for 128 x 128):
+//    partway through slice kt's MFMAs (halfway for 16-bit inputs, three
+//    quarters for fp8) a wait and a barrier free slot kt % NS; the loads of
+//    slice kt + NS into it then go out spread over the next half slice of
+//    MFMAs and have at least NS - 1.5 slices to land before they are
+//    needed.  The next slice's first operand reads follow the barrier,
+//    overlapping the current slice's remaining MFMAs.
 //  * wave-tile MMA: v_mfma_f32_16x16x32_{bf16,f16} (8 x 8 blocks per wave)
 //    and, for the block-scaled path, v_mfma_scale_f32_32x32x64_f8f6f4
 //    (4 x 4 blocks) with the e8m0 block scales as operands (TCGEN05
@@ -240,14 +241,23 @@ struct MNLoader {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+// LDS slots of the K-slice ring.  The 256-row tiles fill the LDS with two
+// (2 x 64 KiB).  A 128 x 128 tile's slice holds a quarter of the MFMA work
+// of a 256 x 256 one, too little to cover the latency of the next slice's
+// loads with one slice in flight, so its ring has four slots (4 x 32 KiB):
+// the loads of slice kt + 4 go out in slice kt, three slices ahead of use.
+template <class T, int TM, int TN>
+constexpr int kSlots = (!T::kScaled && TM * TN <= 128 * 128) ? 4 : 2;
+
 struct Slots {
-  LDS_AS uint8_t *a[2];
-  LDS_AS uint8_t *b[2];
+  LDS_AS uint8_t *a[4];
+  LDS_AS uint8_t *b[4];
   LDS_AS uint8_t *junk;  // 256 bytes per wave: landing area of the L2 prefetches
 };
 
 template <class T, int TM, int TN>
 struct Kernel {
+  static constexpr int kNS = kSlots<T, TM, TN>;
   static constexpr int kElem = T::kElem;
   static constexpr int kWM = TM / 2, kWN = TN / 2;   // wave tile (2 x 2 waves)
   static constexpr int kSlotA = TM * kRowBytes;      // one slot of A, of B (K-major: 64 K rows x 2 TM / 2 TN bytes)
@@ -273,7 +283,7 @@ struct Kernel {
                 "the block-scaled kernel uses 256 x 256 tiles of K-contiguous operands");
   static_assert(kWM % kBlk == 0 && kWN % kBlk == 0, "wave tile");
   // Schedule, in MFMAs of a slice: the wait + barrier go before MFMA
-  // kBarrierAt; the 16 loads of slice kt + 2 go out evenly over the kWindow
+  // kBarrierAt; the loads of slice kt + kNS go out evenly over the kWindow
   // MFMAs from there on (running into slice kt + 1), which leaves
   // kMfma - kWindow MFMAs for the last of them to land.  Loads spread over
   // too short a window overrun the texture unit (about 64 bytes per clock
@@ -305,16 +315,17 @@ struct Kernel {
   static_assert(!kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
   static_assert(kPfHead || kPfAt < kMfma, "prefetch position");
 
-  // Loads of a slice issued in the tail of the slice two before it.
+  // Loads of a slice issued in the tail of the slice kNS before it.
   static constexpr int tail_loads() {
     int n = 0;
     for (int i = 0; i < kLoads; ++i) n += kBarrierAt + i * kWindow / kLoads < kMfma;
     return n;
   }
 
-  // Which load (0..15) of slice kt + 2 (TAIL, positions >= kBarrierAt of
-  // slice kt) or of slice kt + 1 (positions < kBarrierAt of slice kt + 1,
-  // the window's continuation) goes out at MFMA Q; -1 for none.
+  // Which load (0 .. kLoads - 1) of slice kt + kNS (TAIL, positions >=
+  // kBarrierAt of slice kt) or of slice kt + kNS - 1 (positions <
+  // kBarrierAt of slice kt, the continuation of the window opened in slice
+  // kt - 1) goes out at MFMA Q; -1 for none.
   static constexpr int load_at(int Q, bool tail) {
     for (int i = 0; i < kLoads; ++i) {
       const int pos = kBarrierAt + i * kWindow / kLoads;
@@ -488,6 +499,17 @@ struct Kernel {
     (read_one<S, R>(f, sub), ...);
   }
 
+  // Every load of slices 0 .. kNS - 2, slice s into slot s (the prologue).
+  template <int... SL>
+  __device__ __forceinline__ void load_slices(std::integer_sequence<int, SL...>) {
+    (load_slice<SL>(), ...);
+  }
+  template <int SL>
+  __device__ __forceinline__ void load_slice() {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_one<SL>(SL, i);
+  }
+
   // Load instruction i (0 .. kLoads - 1) of slice kt into slot S: A panel,
   // then B.
   template <int S>
@@ -575,10 +597,10 @@ struct Kernel {
   // inside it x block q / kNBm times y block q % kNBm.  Interleaved with it:
   //  * Q < kNR: read Q of substep 1 of this slot into f1;
   //  * before Q = kBarrierAt: wait for this wave's loads of slice kt + 1 and
-  //    synchronise the workgroup (slot kt % 2 is then free);
+  //    synchronise the workgroup (slot kt % kNS is then free);
   //  * from kBarrierAt: reads of substep 0 of slice kt + 1 into f0;
-  //  * the loads of slice kt + 2 into this slot, and the end of those of
-  //    slice kt + 1 into the other slot, as load_at places them.
+  //  * the loads of slice kt + kNS into this slot, and the end of those of
+  //    slice kt + kNS - 1 into the slot before, as load_at places them.
   template <int S, int JB, bool FIRST, int Q>
   __device__ __forceinline__ void mfma_one(int kt, Frags &f0, Frags &f1) {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
@@ -587,8 +609,9 @@ struct Kernel {
     if constexpr (Q == kBarrierAt) {
       // The prefetch issued after the last needed load may be outstanding
       // (none precedes the first slice's barrier in the tail placement).
+      // The loads of slices kt + 2 .. kt + kNS - 1 may be outstanding too.
       constexpr int kPfOut = kPfDist > 0 && (kPfHead || !FIRST) ? 1 : 0;
-      wait_vm_lgkm0<kPfOut>();
+      wait_vm_lgkm0<(kNS - 2) * kLoads + kPfOut>();
       barrier();
       // fp4: the scales of slice kt + 1 into the next set.  An odd slice
       // ends chunk (kt + 1) / 2: the next chunk moves up and the one after
@@ -604,9 +627,9 @@ struct Kernel {
       }
     }
     if constexpr (Q < kNR) read_one<S, Q>(f1, 1);
-    if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNR) read_one<S ^ 1, Q - kBarrierAt>(f0, 0);
-    if constexpr (kHead >= 0) load_one<S ^ 1>(kt + 1, kHead);
-    if constexpr (kTail >= 0) load_one<S>(kt + 2, kTail);
+    if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNR) read_one<(S + 1) % kNS, Q - kBarrierAt>(f0, 0);
+    if constexpr (kHead >= 0) load_one<(S + kNS - 1) % kNS>(kt + kNS - 1, kHead);
+    if constexpr (kTail >= 0) load_one<S>(kt + kNS, kTail);
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
     const Frags &f = SUB == 0 ? f0 : f1;
     if constexpr (T::kDt == kFp4)
@@ -704,12 +727,11 @@ struct Kernel {
       load_chunks(sc_ck, 0);
       load_chunks(sc_ckn, 1);
     }
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_one<0>(0, i);
+    load_slices(std::make_integer_sequence<int, kNS - 1>());
     constexpr int kTailLoads = tail_loads();
 #pragma unroll
-    for (int i = 0; i < kTailLoads; ++i) load_one<1>(1, i);
-    wait_vm_lgkm0<kTailLoads>();
+    for (int i = 0; i < kTailLoads; ++i) load_one<kNS - 1>(kNS - 1, i);
+    wait_vm_lgkm0<(kNS - 2) * kLoads + kTailLoads>();
     if constexpr (T::kScaled) {
       if constexpr (T::kDt == kFp8)
         convert_scales(0);
@@ -733,6 +755,19 @@ struct Kernel {
         step<1, 3>(kt + 2, f0, f1);
         step<0, 0>(kt + 3, f0, f1);
       }
+    } else if constexpr (kNS == 4) {
+      // Four at a time, then the one to three left (no padding: a padded
+      // slice is a quarter of a short K's work).
+      int kt = 1;
+      for (; kt + 3 < nk; kt += 4) {
+        step<1, 1>(kt, f0, f1);
+        step<2, 2>(kt + 1, f0, f1);
+        step<3, 3>(kt + 2, f0, f1);
+        step<0, 0>(kt + 3, f0, f1);
+      }
+      if (kt < nk) step<1, 1>(kt, f0, f1);
+      if (kt + 1 < nk) step<2, 2>(kt + 1, f0, f1);
+      if (kt + 2 < nk) step<3, 3>(kt + 2, f0, f1);
     } else {
       for (int kt = 1; kt < nk; kt += 2) {
         step<1, 1>(kt, f0, f1);
@@ -784,19 +819,15 @@ struct Kernel {
   }
 };
 
-// Workgroups per CU a tile shape is built for: the 256-row shapes fill a
-// SIMD's registers with one wave; 128 x 128 tiles (64 x 64 per wave) leave
-// room for two workgroups per CU, which hide each other's waits.
-template <int TM, int TN>
-constexpr int kWgPerCu = TM * TN <= 128 * 128 ? 2 : 1;
-
+// One workgroup per CU: either shape's ring takes 128 KiB of the 160 KiB
+// LDS, and a 256-row tile's accumulators fill a SIMD's registers.
 template <class T, int TM, int TN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWgPerCu<TM, TN>, kWgPerCu<TM, TN>)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body is device code only; the host pass needs the symbol
-  // Four separate arrays (not one indexed array) so the compiler can tell
-  // the slot being loaded from the slot being read and does not insert a
-  // vmcnt wait in front of every LDS read.
+  // A separate array per slot (not one indexed array) so the compiler can
+  // tell the slot being loaded from the slot being read and does not insert
+  // a vmcnt wait in front of every LDS read.
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TM * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[TM * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TN * kRowBytes];
@@ -807,6 +838,16 @@ void gemm_kernel(const Args a) {
   slots.a[1] = (LDS_AS uint8_t *)sA1;
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
+  if constexpr (kSlots<T, TM, TN> == 4) {
+    __shared__ __attribute__((aligned(1024))) uint8_t sA2[TM * kRowBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA3[TM * kRowBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB2[TN * kRowBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB3[TN * kRowBytes];
+    slots.a[2] = (LDS_AS uint8_t *)sA2;
+    slots.a[3] = (LDS_AS uint8_t *)sA3;
+    slots.b[2] = (LDS_AS uint8_t *)sB2;
+    slots.b[3] = (LDS_AS uint8_t *)sB3;
+  }
   slots.junk = (LDS_AS uint8_t *)junk;
   Kernel<T, TM, TN> k(a, slots);
   k.run();
@@ -844,19 +885,24 @@ hipError_t launch_dt(const Problem &p, const Args &a, int tm, int tn) {
 }
 
 // Tile shapes per kind, largest first, each with a rate relative to
-// 256 x 256 per unit of tile area in a wave of workgroups.  The rates are
-// fitted to sustained measurements on MI355X: 128 x 128 tiles run 4096 x
-// 4096 x 8192 at 0.83 of the 256 x 256 speed but fill the chip for small
-// problems (fp16 NN 1024^3: 11.7 us against 30.8 us; bf16 256^3: 5.8 us
-// against 14.7 us), and 256 x 192 turns 4000 x 3000 x 5000 from 192 into
-// 256 tiles (114 us against 117 us: under the power cap the idle CUs of
-// the smaller grid leave clock headroom, so filling them gains little).
+// 256 x 256 per unit of tile area in a wave of workgroups (one workgroup
+// per CU).  The rates are fitted to sustained measurements on MI355X
+// (bf16 NT unless noted, us):
+//                        256x256  256x192  128x128
+//   4096 x 4096 x 8192     193      --       251    (rate 0.77 here)
+//   3072 x 3072 x 3072      65      --        74
+//   4000 x 3000 x 5000     118     117       156
+//   2048 x 2048 x 4096      78      63        35
+//   2048 x 1024 x 4096      77      --        27
+//   fp16 NN 1024^3          31      --        11.8
+// 0.70 for 128 x 128 sits between the first two rows: a partly filled last
+// wave runs at a higher clock under the power cap than whole ones.
 struct Shape {
   int tm, tn;
   double rel;
 };
-constexpr Shape kShapesBK[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.45}};  // B K-contiguous
-constexpr Shape kShapesBN[] = {{256, 256, 1.0}, {128, 128, 0.45}};                     // B N-contiguous
+constexpr Shape kShapesBK[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.70}};  // B K-contiguous
+constexpr Shape kShapesBN[] = {{256, 256, 1.0}, {128, 128, 0.70}};                     // B N-contiguous
 
 // The shape with the least estimated time: whole waves of tiles over the
 // CUs, each wave costing its tile area over the shape's relative rate.
@@ -867,7 +913,7 @@ Shape pick_shape(const Shape (&shapes)[NS], int64_t M, int64_t N, int cus) {
   for (size_t i = 0; i < NS; ++i) {
     const Shape &s = shapes[i];
     const int64_t tiles = ((M + s.tm - 1) / s.tm) * ((N + s.tn - 1) / s.tn);
-    const int64_t slots = (int64_t)cus * (s.tm * s.tn <= 128 * 128 ? 2 : 1);
+    const int64_t slots = cus;  // one workgroup per CU
     const int64_t waves = (tiles + slots - 1) / slots;
     const double t = (double)waves * s.tm * s.tn / s.rel;
     if (i == 0 || t < best_t) {
