@@ -71,6 +71,15 @@ def _load():
     lib.oracle_gemm_mxfp4_nt.restype = None
     lib.oracle_gemm_mxfp4_nt_at.argtypes = [i64, i64, i64, u8p, u8p, u8p, u8p, i64, i64p, i64p, u16p, f64p]
     lib.oracle_gemm_mxfp4_nt_at.restype = None
+    lib.oracle_decode_fp6.argtypes = [i64, u8p, ctypes.c_int, f64p]
+    lib.oracle_decode_fp6.restype = None
+    lib.oracle_unpack_fp6.argtypes = [i64, i64, i64, u8p, u8p]
+    lib.oracle_unpack_fp6.restype = None
+    lib.oracle_gemm_mxfp6_nt.argtypes = [i64, i64, i64, ctypes.c_int, u8p, u8p, u8p, u8p, u16p, f64p]
+    lib.oracle_gemm_mxfp6_nt.restype = None
+    lib.oracle_gemm_mxfp6_nt_at.argtypes = [i64, i64, i64, ctypes.c_int, u8p, u8p, u8p, u8p, i64, i64p, i64p,
+                                            u16p, f64p]
+    lib.oracle_gemm_mxfp6_nt_at.restype = None
     lib.oracle_quantize_mxfp8.argtypes = [i64, i64, ctypes.c_void_p, u8p, u8p]
     lib.oracle_quantize_mxfp8.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -310,4 +319,69 @@ def gemm_mxfp4_nt_at(qA, qB, sA, sB, rows, cols, K=None, want_f64: bool = False)
     out64 = np.empty(rows.size, np.float64) if want_f64 else None
     _load().oracle_gemm_mxfp4_nt_at(M, N, K, _ptr(qA), _ptr(qB), _ptr(sA), _ptr(sB), rows.size,
                                     _ptr(rows), _ptr(cols), _ptr(out), _ptr(out64))
+    return (out, out64) if want_f64 else out
+
+
+# --- MXFP6 ---------------------------------------------------------------------
+
+FP6_FORMATS = {"e2m3": 0, "e3m2": 1}
+
+
+def decode_fp6(codes, fmt: str) -> np.ndarray:
+    """FP6 codes (0..63, one per byte) of element type fmt ("e2m3" or
+    "e3m2") -> float64."""
+    b = _c(np.asarray(codes, np.uint8), np.uint8)
+    out = np.empty(b.shape, np.float64)
+    _load().oracle_decode_fp6(b.size, _ptr(b), FP6_FORMATS[fmt], _ptr(out))
+    return out
+
+
+def unpack_fp6(q, K: int) -> np.ndarray:
+    """Packed FP6 rows (R, 3K/4) -> codes (R, K), as the GEMM reads them."""
+    q = _c(q, np.uint8)
+    R, RB = q.shape
+    if K % 4 or RB != K // 4 * 3:
+        raise ValueError("rows must hold 3K/4 bytes, K % 4 == 0")
+    out = np.empty((R, K), np.uint8)
+    _load().oracle_unpack_fp6(R, RB, K, _ptr(q), _ptr(out))
+    return out
+
+
+def _mxfp6_shapes(qA, qB, sA, sB, K):
+    (M, RB), (N, RB2) = qA.shape, qB.shape
+    if K is None:
+        K = RB // 3 * 4
+    KB = (K + 31) // 32
+    if K % 4 or RB != K // 4 * 3 or RB2 != RB or sA.shape != (M, KB) or sB.shape != (N, KB):
+        raise ValueError("operand shapes do not match")
+    return M, N, K
+
+
+def gemm_mxfp6_nt(qA, qB, sA, sB, fmt: str, K=None, want_f64: bool = False):
+    """Block-scaled FP6 NT GEMM -> C (M,N) bf16 bits.
+
+    qA (M,3K/4), qB (N,3K/4): FP6 elements of type fmt ("e2m3" or "e3m2")
+    packed densely, element k at bits 6k .. 6k+5 of the row (little-endian);
+    sA (M,ceil(K/32)), sB (N,ceil(K/32)): e8m0 bytes, one per row per 32 K.
+    """
+    qA, qB, sA, sB = (_c(x, np.uint8) for x in (qA, qB, sA, sB))
+    M, N, K = _mxfp6_shapes(qA, qB, sA, sB, K)
+    C = np.empty((M, N), np.uint16)
+    C64 = np.empty((M, N), np.float64) if want_f64 else None
+    _load().oracle_gemm_mxfp6_nt(M, N, K, FP6_FORMATS[fmt], _ptr(qA), _ptr(qB), _ptr(sA), _ptr(sB), _ptr(C),
+                                 _ptr(C64))
+    return (C, C64) if want_f64 else C
+
+
+def gemm_mxfp6_nt_at(qA, qB, sA, sB, rows, cols, fmt: str, K=None, want_f64: bool = False):
+    """C[rows[p], cols[p]] of the block-scaled FP6 NT GEMM (bf16 bits)."""
+    qA, qB, sA, sB = (_c(x, np.uint8) for x in (qA, qB, sA, sB))
+    M, N, K = _mxfp6_shapes(qA, qB, sA, sB, K)
+    rows, cols = _points(rows, cols)
+    if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+        raise ValueError("bad sample positions")
+    out = np.empty(rows.size, np.uint16)
+    out64 = np.empty(rows.size, np.float64) if want_f64 else None
+    _load().oracle_gemm_mxfp6_nt_at(M, N, K, FP6_FORMATS[fmt], _ptr(qA), _ptr(qB), _ptr(sA), _ptr(sB),
+                                    rows.size, _ptr(rows), _ptr(cols), _ptr(out), _ptr(out64))
     return (out, out64) if want_f64 else out

@@ -486,6 +486,114 @@ void oracle_decode_e2m1(int64_t n, const uint8_t *nibbles, double *out)
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_to_f64(nibbles[i] & 15);
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP6                                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * OCP FP6 elements (the MXFP6 element types), from their definitions:
+ *   fmt 0, E2M3: sign, 2 exponent bits (bias 1), 3 mantissa bits; max 7.5;
+ *   fmt 1, E3M2: sign, 3 exponent bits (bias 3), 2 mantissa bits; max 28.
+ * Exponent field 0 is subnormal: mantissa * 2^(1 - bias - mantissa bits).
+ * Neither type has infinities or NaN.
+ */
+double oracle_fp6_to_f64(uint8_t code, int fmt)
+{
+    const int ebits = fmt == 0 ? 2 : 3, mbits = 5 - ebits, bias = fmt == 0 ? 1 : 3;
+    const int sign = (code >> 5) & 1;
+    const int e = (code >> mbits) & ((1 << ebits) - 1);
+    const int f = code & ((1 << mbits) - 1);
+    double v = e == 0 ? ldexp((double)f, 1 - bias - mbits)
+                      : ldexp((double)((1 << mbits) + f), e - bias - mbits);
+    return sign ? -v : v;
+}
+
+/*
+ * Element k of a row of packed FP6: bits 6k .. 6k + 5 of the row read as a
+ * little-endian bit string (byte b holds bits 8b .. 8b + 7, bit 0 its least
+ * significant).  The second byte is read only when the element reaches it.
+ */
+static uint8_t fp6_at(const uint8_t *row, int64_t k)
+{
+    const int64_t bit = 6 * k, byte = bit / 8;
+    const int sh = (int)(bit % 8);
+    unsigned v = row[byte] >> sh;
+    if (sh > 2) v |= (unsigned)row[byte + 1] << (8 - sh);
+    return (uint8_t)(v & 63u);
+}
+
+/*
+ * MXFP6 NT: C[m][n] = R_bf16( sum_k (fp6(A[m][k]) * 2^(EA[m][k/32]-127))
+ *                                  * (fp6(B[n][k]) * 2^(EB[n][k/32]-127)) ),
+ * both operands of element type fmt.  Another of the block-scaled formats
+ * the Blackwell TCGEN05 GEMM tutorial (section "进阶" (Advanced)) groups
+ * with MXFP8; the pages give no layout, so this follows the OCP MX format
+ * (one E8M0 scale per 32 consecutive elements along K) with the elements
+ * packed densely: a row of K elements is 3K/4 bytes, element k at bits
+ * 6k .. 6k + 5.  K % 4 == 0; sA is M x ceil(K/32).
+ */
+void oracle_gemm_mxfp6_nt(int64_t M, int64_t N, int64_t K, int fmt,
+                          const uint8_t *qA, const uint8_t *qB,
+                          const uint8_t *sA, const uint8_t *sB,
+                          uint16_t *C, double *C64)
+{
+    const int64_t KB = (K + 31) / 32, RB = K / 4 * 3;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = oracle_fp6_to_f64(fp6_at(qA + m * RB, k), fmt) *
+                           oracle_e8m0_to_f64(sA[m * KB + k / 32]);
+                double b = oracle_fp6_to_f64(fp6_at(qB + n * RB, k), fmt) *
+                           oracle_e8m0_to_f64(sB[n * KB + k / 32]);
+                acc += a * b;
+            }
+            if (C64) C64[m * N + n] = acc;
+            if (C) C[m * N + n] = oracle_f64_to_bf16(acc);
+        }
+    }
+}
+
+/* Chosen outputs C[rows[p]][cols[p]] of oracle_gemm_mxfp6_nt. */
+void oracle_gemm_mxfp6_nt_at(int64_t M, int64_t N, int64_t K, int fmt,
+                             const uint8_t *qA, const uint8_t *qB,
+                             const uint8_t *sA, const uint8_t *sB,
+                             int64_t P, const int64_t *rows, const int64_t *cols,
+                             uint16_t *out, double *out64)
+{
+    (void)M; (void)N;
+    const int64_t KB = (K + 31) / 32, RB = K / 4 * 3;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t m = rows[p], n = cols[p];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = oracle_fp6_to_f64(fp6_at(qA + m * RB, k), fmt) *
+                       oracle_e8m0_to_f64(sA[m * KB + k / 32]);
+            double b = oracle_fp6_to_f64(fp6_at(qB + n * RB, k), fmt) *
+                       oracle_e8m0_to_f64(sB[n * KB + k / 32]);
+            acc += a * b;
+        }
+        if (out64) out64[p] = acc;
+        if (out) out[p] = oracle_f64_to_bf16(acc);
+    }
+}
+
+/* fp6 codes (one per byte, low 6 bits) -> binary64. */
+void oracle_decode_fp6(int64_t n, const uint8_t *codes, int fmt, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp6_to_f64(codes[i] & 63, fmt);
+}
+
+/* Element k of each of n packed FP6 rows of `row_bytes` bytes -> codes (the
+ * oracle's unpacking, exposed so a test can check the bit order). */
+void oracle_unpack_fp6(int64_t rows, int64_t row_bytes, int64_t K, const uint8_t *q, uint8_t *codes)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) codes[r * K + k] = fp6_at(q + r * row_bytes, k);
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_num_threads(void)
 {

@@ -30,6 +30,21 @@ FP4_BLOCK_K = 32                     # OCP MX block: one scale per 32 elements
 FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
+def _fp6_grid(ebits: int, bias: int) -> np.ndarray:
+    """Magnitudes of the 32 non-negative OCP FP6 codes, in code order
+    (exponent field 0 subnormal; no infinities or NaN)."""
+    mbits = 5 - ebits
+    out = []
+    for c in range(32):
+        e, f = c >> mbits, c & ((1 << mbits) - 1)
+        out.append(math.ldexp(f, 1 - bias - mbits) if e == 0 else math.ldexp((1 << mbits) + f, e - bias - mbits))
+    return np.array(out)
+
+
+# OCP FP6 element types: name -> (magnitude grid, largest value).
+FP6 = {"e2m3": (_fp6_grid(2, 1), 7.5), "e3m2": (_fp6_grid(3, 3), 28.0)}
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
@@ -60,6 +75,8 @@ WORKLOADS = {
         # The step before the block-scaled GEMM: one of its operands, quantised.
         Workload("mxfp4_nt_4096", "mxfp4_nt", 4096, 4096, 4096,
                  "block-scaled fp4 (e2m1 + e8m0 per 32 K) NT GEMM M=N=K=4096"),
+        Workload("mxfp6_e2m3_nt_4096", "mxfp6_e2m3_nt", 4096, 4096, 4096,
+                 "block-scaled fp6 (e2m3 + e8m0 per 32 K) NT GEMM M=N=K=4096"),
         Workload("quant_mxfp8_4096", "quant_mxfp8", 4096, 0, 4096,
                  "block-scale quantiser fp32 -> e4m3fn + e8m0 per 128 K, M=K=4096"),
     )
@@ -144,6 +161,55 @@ def quantize_mxfp4(x: torch.Tensor):
     return pack_fp4(code), (e + 127).astype(np.uint8)
 
 
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """FP6 codes (R, K), K % 4 == 0 -> bytes (R, 3K/4): element k at bits
+    6k .. 6k + 5 of the row read as a little-endian bit string."""
+    c = codes.astype(np.uint32)
+    R, K = c.shape
+    v = c[:, 0::4] | (c[:, 1::4] << 6) | (c[:, 2::4] << 12) | (c[:, 3::4] << 18)   # 24 bits per 4 elements
+    out = np.empty((R, K // 4, 3), np.uint8)
+    out[:, :, 0] = v & 255
+    out[:, :, 1] = (v >> 8) & 255
+    out[:, :, 2] = v >> 16
+    return out.reshape(R, K // 4 * 3)
+
+
+def quantize_mxfp6(x: torch.Tensor, fmt: str):
+    """Quantise float32 rows (R, K), K % 32 == 0, to packed FP6 of element
+    type fmt ("e2m3" or "e3m2") with one e8m0 scale per 32 K elements: the
+    smallest 2^e with absmax <= MAX * 2^e (MAX = 7.5 or 28; the rule of the
+    other block-scaled inputs), then each x * 2^-e rounded to the nearest
+    FP6 value, ties to the even code.  Returns (q uint8 (R, 3K/4), scales
+    uint8 (R, K/32))."""
+    grid, vmax = FP6[fmt]
+    xr = x.double()                                           # torch: its elementwise ops use every core
+    R, K = xr.shape
+    KB = K // FP4_BLOCK_K
+    blocks = xr.reshape(R, KB, FP4_BLOCK_K)
+    absmax = blocks.abs().amax(dim=2)
+    frac, exp = torch.frexp(absmax)                           # absmax = frac * 2^exp, frac in [0.5, 1)
+    mfrac, mexp = math.frexp(vmax)                            # vmax = mfrac * 2^mexp
+    # absmax / 2^(exp - mexp) = 2^mexp frac <= vmax iff frac <= mfrac.
+    e = exp.long() - mexp + (frac > mfrac).long()
+    e = torch.where(absmax == 0.0, torch.full_like(e, -127), e).clamp(-127, 127)
+    y = (blocks * torch.exp2(-e.double())[:, :, None]).reshape(R, K)   # exact power-of-two scaling
+    a = y.abs()
+    gt = torch.from_numpy(grid)
+    lo = (torch.bucketize(a, gt, right=True) - 1).clamp(0, 31)
+    hi = (lo + 1).clamp(max=31)
+    dlo, dhi = a - gt[lo], gt[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0) & (hi != lo))
+    code = torch.where(pick_hi, hi, lo) | ((torch.signbit(y) & (a > 0)).long() << 5)
+    e = e.numpy()
+    code = code.numpy()
+    return pack_fp6(code), (e + 127).astype(np.uint8)
+
+
+def fp6_format(kind: str) -> str:
+    """"mxfp6_e2m3_nt" -> "e2m3"."""
+    return kind.split("_")[1]
+
+
 def make_inputs(w: Workload | str, seed: int = 0):
     """Inputs of a workload as a dict of numpy bit-pattern arrays.
 
@@ -177,6 +243,12 @@ def make_random(kind: str, M: int, N: int, K: int, seed: int = 0):
         qA, sA = quantize_mxfp8(a)
         qB, sB = quantize_mxfp8(b)
         return {"qA": qA, "qB": qB, "sA": sA, "sB": sB}
+    if kind in ("mxfp6_e2m3_nt", "mxfp6_e3m2_nt"):
+        a = randn_f32((M, K), g)
+        b = randn_f32((N, K), g)
+        qA, sA = quantize_mxfp6(a, fp6_format(kind))
+        qB, sB = quantize_mxfp6(b, fp6_format(kind))
+        return {"qA": qA, "qB": qB, "sA": sA, "sB": sB}
     raise ValueError(kind)
 
 
@@ -203,6 +275,16 @@ def make_integer(kind: str, M: int, N: int, K: int, seed: int = 0, lo: int = -2,
         KB = K // FP4_BLOCK_K
         qA = pack_fp4(lut[ints((M, K)).numpy().astype(np.int64) + 2])
         qB = pack_fp4(lut[ints((N, K)).numpy().astype(np.int64) + 2])
+        return {"qA": qA, "qB": qB, "sA": np.full((M, KB), 127, np.uint8), "sB": np.full((N, KB), 127, np.uint8)}
+    if kind in ("mxfp6_e2m3_nt", "mxfp6_e3m2_nt"):
+        # Integers in [lo, hi] are exact in both FP6 types; their codes are
+        # found on the type's own grid (sign bit 32).
+        grid = FP6[fp6_format(kind)][0]
+        lut = np.array([int(np.flatnonzero(grid == abs(v))[0]) | (32 if v < 0 else 0) for v in range(-2, 3)],
+                       np.uint8)
+        KB = K // FP4_BLOCK_K
+        qA = pack_fp6(lut[ints((M, K)).numpy().astype(np.int64) + 2])
+        qB = pack_fp6(lut[ints((N, K)).numpy().astype(np.int64) + 2])
         return {"qA": qA, "qB": qB, "sA": np.full((M, KB), 127, np.uint8), "sB": np.full((N, KB), 127, np.uint8)}
     if kind == "mxfp8_nt":
         KB = (K + SCALE_BLOCK_K - 1) // SCALE_BLOCK_K
