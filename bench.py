@@ -50,7 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "mxfp8": 5033.2, "mxfp4": 10066.3}  # MI355X dense MFMA, 256 CU x 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "mxfp8": 5033.2, "mxfp4": 10066.3, "mxfp6": 10066.3}  # MI355X dense MFMA, 256 CU x 2.4 GHz
 METRIC = "TFLOPS (2MNK/t) and % of MFMA peak, bf16 NT GEMM 4096x4096x8192, 1 GPU"
 CSRC = os.path.join(ROOT, "dense_tiled_gemm_bf16_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "tgemm_kernels.hip")        # the GEMM kernels
@@ -120,6 +120,11 @@ def launcher(w, dev, out, stream):
     elif w.kind == "f16_nn":
         args = (M, N, K, dev["A"].data_ptr(), dev["B"].data_ptr(), out.data_ptr(), s)
         fn = L.gemm_f16_nn
+    elif w.kind.startswith("mxfp6"):
+        fmt = {"mxfp6_e2m3_nt": 0, "mxfp6_e3m2_nt": 1}[w.kind]
+        args = (fmt, M, N, K, dev["qA"].data_ptr(), dev["qB"].data_ptr(), dev["sA"].data_ptr(),
+                dev["sB"].data_ptr(), out.data_ptr(), s)
+        fn = L.gemm_mxfp6_nt
     else:
         args = (M, N, K, dev["qA"].data_ptr(), dev["qB"].data_ptr(), dev["sA"].data_ptr(),
                 dev["sB"].data_ptr(), out.data_ptr(), s)
@@ -146,6 +151,9 @@ def parity_sample(w, x, out):
         ref = oracle.gemm_f16_nn_at(x["A"], x["B"], rows, cols)
     elif w.kind == "mxfp4_nt":
         ref = oracle.gemm_mxfp4_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols)
+    elif w.kind.startswith("mxfp6"):
+        ref = oracle.gemm_mxfp6_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols,
+                                      workloads.fp6_format(w.kind))
     else:
         ref = oracle.gemm_mxfp8_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols)
     dt = torch.float16 if w.kind == "f16_nn" else torch.bfloat16
@@ -174,6 +182,8 @@ def cpu_baseline(w, x, target_s: float):
             oracle.gemm_f16_nn_at(x["A"], x["B"], rows, cols)
         elif w.kind == "mxfp4_nt":
             oracle.gemm_mxfp4_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols)
+        elif w.kind.startswith("mxfp6"):
+            oracle.gemm_mxfp6_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols, workloads.fp6_format(w.kind))
         else:
             oracle.gemm_mxfp8_nt_at(x["qA"], x["qB"], x["sA"], x["sB"], rows, cols)
         return time.perf_counter() - t0
@@ -245,7 +255,7 @@ def record_traffic(d: str, name: str):
     if quant:
         alg = quant_bytes(w)
     else:
-        per_elem = {"mxfp8_nt": 1.0, "mxfp4_nt": 0.5}.get(w.kind, 2.0)
+        per_elem = {"mxfp8_nt": 1.0, "mxfp4_nt": 0.5, "mxfp6_e2m3_nt": 0.75, "mxfp6_e3m2_nt": 0.75}.get(w.kind, 2.0)
         in_bytes = int((w.M + w.N) * w.K * per_elem)
         alg = in_bytes + w.M * w.N * 2
     rec = {"workload": name, "kernel_source_sha256_16": kernel_source_hash(src=source_of(w.kind)),
@@ -378,7 +388,8 @@ def main():
     if w.kind == "quant_mxfp8":
         bench_quantize(args, w)
         return
-    prec = {"bf16_nt": "bf16", "f16_nn": "f16", "mxfp8_nt": "mxfp8", "mxfp4_nt": "mxfp4"}[w.kind]
+    prec = {"bf16_nt": "bf16", "f16_nn": "f16", "mxfp8_nt": "mxfp8", "mxfp4_nt": "mxfp4",
+            "mxfp6_e2m3_nt": "mxfp6", "mxfp6_e3m2_nt": "mxfp6"}[w.kind]
     torch.cuda.set_device(0)
     tg.init()
     tile = None
@@ -445,7 +456,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f16": "f16", "mxfp8": "fp8e4m3+e8m0", "mxfp4": "fp4e2m1+e8m0"}[prec],
+        "dtype": {"bf16": "bf16", "f16": "f16", "mxfp8": "fp8e4m3+e8m0", "mxfp4": "fp4e2m1+e8m0",
+                  "mxfp6": f"fp6{workloads.fp6_format(w.kind) if prec == 'mxfp6' else ''}+e8m0"}[prec],
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "layout": "NT" if w.kind != "f16_nn" else "NN",

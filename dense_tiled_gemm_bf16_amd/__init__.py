@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_mxfp8_nt.argtypes = [i64, i64, i64, p, p, p, p, p, p]
     L.gemm_mxfp4_nt.argtypes = [i64, i64, i64, p, p, p, p, p, p]
     L.gemm_mxfp4_nt.restype = ctypes.c_int
+    L.gemm_mxfp6_nt.argtypes = [ctypes.c_int, i64, i64, i64, p, p, p, p, p, p]
+    L.gemm_mxfp6_nt.restype = ctypes.c_int
     for f in (L.gemm_bf16_nt, L.gemm_f16_nn, L.gemm_mxfp8_nt):
         f.restype = ctypes.c_int
     L.tgemm_init.argtypes = []
@@ -233,5 +235,31 @@ def gemm_mxfp4_nt(a, b, scale_a, scale_b, out=None, stream=None):
     _want(scale_b, "scale_b", torch.uint8, (N, K // 32))
     c = _out(out, (M, N), torch.bfloat16, a)
     check(lib().gemm_mxfp4_nt(M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
+                              scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    return c
+
+
+FP6_FORMATS = {"e2m3": 0, "e3m2": 1}   # TGEMM_FP6_E2M3, TGEMM_FP6_E3M2
+
+
+def gemm_mxfp6_nt(a, b, scale_a, scale_b, fmt="e2m3", out=None, stream=None):
+    """Block-scaled FP6 NT GEMM -> bf16 (M,N).
+
+    a (M,3K/4), b (N,3K/4): FP6 elements of type fmt ("e2m3" or "e3m2")
+    packed densely (element k at bits 6k .. 6k+5 of the row, little-endian),
+    uint8; scale_a (M,K/32), scale_b (N,K/32): e8m0 bytes.  K % 64 == 0.
+    """
+    torch = _torch()
+    M, RB = a.shape
+    N = b.shape[0]
+    K = RB // 3 * 4
+    if fmt not in FP6_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FP6_FORMATS)}")
+    _want(a, "a", torch.uint8, (M, RB))
+    _want(b, "b", torch.uint8, (N, RB))
+    _want(scale_a, "scale_a", torch.uint8, (M, K // 32))
+    _want(scale_b, "scale_b", torch.uint8, (N, K // 32))
+    c = _out(out, (M, N), torch.bfloat16, a)
+    check(lib().gemm_mxfp6_nt(FP6_FORMATS[fmt], M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
                               scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
     return c

@@ -214,6 +214,29 @@ int gemm_mxfp4_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
   return dispatch(fn, p);
 }
 
+int gemm_mxfp6_nt(int fmt, int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *scale_A,
+                  const void *scale_B, void *C, hipStream_t stream) {
+  static const char fn[] = "gemm_mxfp6_nt";
+  g_err[0] = '\0';
+  if (fmt != TGEMM_FP6_E2M3 && fmt != TGEMM_FP6_E3M2)
+    return fail(TGEMM_EINVAL, "%s: fmt=%d must be TGEMM_FP6_E2M3 (0) or TGEMM_FP6_E3M2 (1)", fn, fmt);
+  const uint64_t m = M > 0 ? (uint64_t)M : 0, n = N > 0 ? (uint64_t)N : 0, k = K > 0 ? (uint64_t)K : 0;
+  const uint64_t kb = (k + 31) / 32, row = k / 4 * 3;
+  const Operand ops[] = {{"A", A, m * row, true},
+                         {"B", B, n * row, true},
+                         {"scale_A", scale_A, m * kb, false},
+                         {"scale_B", scale_B, n * kb, false}};
+  int rc = check_common(fn, M, N, K, 64, ops, 4, C, m * n * 2);
+  if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
+  if ((uint64_t)tgemm::kTileM * row > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * 3K/4 bytes must stay below 2^31)", fn, (long long)K);
+  if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
+  const tgemm::Dt dt = fmt == TGEMM_FP6_E2M3 ? tgemm::Dt::kMxfp6E2M3 : tgemm::Dt::kMxfp6E3M2;
+  tgemm::Problem p{dt, false, true, M, N, K, A, K / 4 * 3, B, K / 4 * 3, scale_A, scale_B, C, N, stream, 0, 0, 0};
+  return dispatch(fn, p);
+}
+
 int gemm_bf16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
   return gemm_general("gemm_bf16", tgemm::Dt::kBf16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, stream);

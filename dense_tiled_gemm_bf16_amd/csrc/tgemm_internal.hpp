@@ -8,7 +8,7 @@
 namespace tgemm {
 
 // Element type of A and B (C is bf16, or fp16 for fp16 inputs).
-enum class Dt : int { kBf16 = 0, kF16 = 1, kMxfp8 = 2, kMxfp4 = 3 };
+enum class Dt : int { kBf16 = 0, kF16 = 1, kMxfp8 = 2, kMxfp4 = 3, kMxfp6E2M3 = 4, kMxfp6E3M2 = 5 };
 
 // A validated problem, C = op(A) op(B): sizes are non-negative and fit the
 // kernels' limits, pointers and row strides are aligned, M > 0 and N > 0.

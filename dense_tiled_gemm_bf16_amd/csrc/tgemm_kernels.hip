@@ -92,13 +92,17 @@ struct Args {
 // (K-contiguous; else K x M); BK, B is N x K (K-contiguous; else K x N).
 // fp4 operands are handled as rows of bytes (two E2M1 elements each):
 // kElem = 1 and K counts bytes inside the kernel.
-enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2, kFp4 = 3 };
+// fp6 (E2M3 or E3M2) likewise: rows of densely packed 6-bit elements, K
+// counted in bytes, 96 bytes (128 elements, two MFMA K steps) per slice.
+enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2, kFp4 = 3, kFp6E2M3 = 4, kFp6E3M2 = 5 };
 template <int DT, bool AK, bool BK>
 struct Traits {
   static constexpr int kDt = DT;
-  static constexpr int kElem = DT == kFp8 || DT == kFp4 ? 1 : 2;
+  static constexpr bool kScaled = DT >= kFp8;
+  static constexpr bool kFp6 = DT == kFp6E2M3 || DT == kFp6E3M2;
+  static constexpr int kElem = kScaled ? 1 : 2;
+  static constexpr int kSliceBytes = kFp6 ? 96 : 128;  // global bytes of a row per K slice
   static constexpr bool kAK = AK, kBK = BK;
-  static constexpr bool kScaled = DT == kFp8 || DT == kFp4;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -177,16 +181,22 @@ struct PanelLoader {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t off[NI];  // per instruction: byte offset of this lane's chunk at slice 0
   int kcol[2];       // element column of this lane's chunk inside a slice (even / odd i)
+  uint32_t slice_bytes;
 
-  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int ld, int elem, int wave,
-                                       int lane) {
+  // slice_k: elements of a row per slice (fp6: 96 bytes, so the slot
+  // rows' last two chunks stay unloaded).
+  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int ld, int elem, int slice_k,
+                                       int wave, int lane) {
+    slice_bytes = (uint32_t)(slice_k * elem);
     rsrc = make_rsrc(panel, ((uint32_t)(rows_valid - 1) * (uint32_t)ld + (uint32_t)K) * (uint32_t)elem);
 #pragma unroll
     for (int p = 0; p < 2; ++p) kcol[p] = ((lane & 7) ^ swz(8 * p + (lane >> 3))) * (16 / elem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = wave * 8 * NI + i * 8 + (lane >> 3);
-      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)ld * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem : kOOB;
+      off[i] = r < rows_valid && kcol[i & 1] < slice_k
+                   ? (uint32_t)r * (uint32_t)ld * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem
+                   : kOOB;
     }
   }
 
@@ -195,7 +205,7 @@ struct PanelLoader {
   __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k, int i) const {
     const bool ok = kt * slice_k + kcol[i & 1] < K;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
-                                             ok ? off[i] : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
+                                             ok ? off[i] : kOOB, (uint32_t)kt * slice_bytes, 0, 0);
   }
 };
 
@@ -262,7 +272,7 @@ struct Kernel {
   static constexpr int kWM = TM / 2, kWN = TN / 2;   // wave tile (2 x 2 waves)
   static constexpr int kSlotA = TM * kRowBytes;      // one slot of A, of B (K-major: 64 K rows x 2 TM / 2 TN bytes)
   static constexpr int kSlotB = TN * kRowBytes;
-  static constexpr int kSliceK = kRowBytes / kElem;  // K elements per slice
+  static constexpr int kSliceK = T::kSliceBytes / kElem;  // K elements (packed kinds: bytes) per slice
   // MFMA shape.  16-bit inputs: v_mfma_f32_16x16x32 (it reads and writes 4
   // accumulators per 16 K flops, half the accumulator traffic per flop of
   // the 32 x 32 x 16 form; under full load the chip is power-capped, and the
@@ -382,7 +392,22 @@ struct Kernel {
   // Fragment of one block of kBlk rows (B rows = C columns for x, A rows for
   // y), K substep `sub`, from a K-contiguous slot.
   __device__ __forceinline__ Frag read_rows(const LDS_AS uint8_t *slot, int row0, int sub) const {
-    if constexpr (kW) {
+    if constexpr (T::kFp6) {
+      // 32 x 32 x 64 on fp6: lane l holds row l % 32 and 24 bytes (32
+      // elements) of K: bytes 48 sub + 24 (l / 32) .. + 23, read as three
+      // 8-byte pieces (a 16-byte chunk holds two).  Registers 6 and 7 are
+      // not used by the MFMA.
+      const LDS_AS uint8_t *p = slot + (row0 + (lane & 31)) * kRowBytes;
+      i32x8 r = {};
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int b = 48 * sub + 24 * (lane >> 5) + 8 * q;
+        const u32x2 v = *(const LDS_AS u32x2 *)(p + ((((b >> 4) ^ lane_sw) << 4) | (b & 8)));
+        r[2 * q] = (int)v[0];
+        r[2 * q + 1] = (int)v[1];
+      }
+      return r;
+    } else if constexpr (kW) {
       // 32 x 32 x 64: lane l holds row l % 32 and 32 bytes of K: logical
       // chunks 4 sub + 2 (l / 32) and the one after.
       const int c = 4 * sub + 2 * (lane >> 5);
@@ -456,6 +481,14 @@ struct Kernel {
       // Format code 0 (OCP FP8 E4M3) for both operands; byte SEL of each
       // scale VGPR (the slice's place in its group of 4).
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, SEL, sx, SEL, sy);
+    } else if constexpr (T::kFp6) {
+      // Format code 2 (OCP FP6 E2M3) or 3 (E3M2): 24 bytes, 32 elements per
+      // lane, in the fragment's first six registers; byte SEL of each scale
+      // VGPR (the K step).
+      constexpr int F = T::kDt == kFp6E2M3 ? 2 : 3;
+      const i32x8 x6 = {x[0], x[1], x[2], x[3], x[4], x[5], 0, 0};
+      const i32x8 y6 = {y[0], y[1], y[2], y[3], y[4], y[5], 0, 0};
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x6, y6, c, F, F, SEL, sx, SEL, sy);
     } else {
       // Format code 4 (OCP FP4 E2M1): 16 bytes, 32 elements per lane, taken
       // from half H of the fragment (the compiler reads the 4 registers in
@@ -532,7 +565,7 @@ struct Kernel {
   __device__ __forceinline__ void prefetch(int kt) {
     const bool ok = kt * kSliceK < a.K;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (LDS_AS void *)(slots.junk + wave * 256), 4,
-                                             ok ? pf_off : kOOB, (uint32_t)kt * kRowBytes, 0, 0);
+                                             ok ? pf_off : kOOB, (uint32_t)kt * T::kSliceBytes, 0, 0);
   }
 
   // Chunk c of every instruction's row into dst.  The resource ends at the
@@ -593,6 +626,28 @@ struct Kernel {
     if ((g & 3) == 3) load_chunks(sc_ckn, (g >> 2) + 2);
   }
 
+  // fp6: slice t's 4 scale bytes per row (groups 0-3 of its 128 elements),
+  // shifted out of the window's first two dwords; the MFMA of K step s, in
+  // wave half w, uses group 2 s + w, so lanes 0-31 take groups 0, 2 and
+  // lanes 32-63 groups 1, 3, in byte s.  The window then moves on by one
+  // dword; once it has moved a whole chunk the chunk after the next is
+  // loaded (waited for by the next barrier, used after it).
+  __device__ __forceinline__ void convert_scales6(int t) {
+    const uint32_t keep = keep_mask(a.kb - 4 * t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d = __builtin_amdgcn_alignbyte(sc_ck[j][1], sc_ck[j][0], sc_sh[j]) & keep;
+      const uint32_t lo = __builtin_amdgcn_perm(0u, d, 0x0c0c0200u);  // groups 0, 2
+      const uint32_t hi = __builtin_amdgcn_perm(0u, d, 0x0c0c0301u);  // groups 1, 3
+      const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+      sc_nxt[2 * j] = (int)sw[0];
+      sc_nxt[2 * j + 1] = (int)sw[1];
+      sc_ck[j] = u32x4{sc_ck[j][1], sc_ck[j][2], sc_ck[j][3], sc_ckn[j][0]};
+      sc_ckn[j] = u32x4{sc_ckn[j][1], sc_ckn[j][2], sc_ckn[j][3], 0u};
+    }
+    if ((t & 3) == 3) load_chunks(sc_ckn, (t >> 2) + 2);
+  }
+
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
   // inside it x block q / kNBm times y block q % kNBm.  Interleaved with it:
   //  * Q < kNR: read Q of substep 1 of this slot into f1;
@@ -617,6 +672,7 @@ struct Kernel {
       // ends chunk (kt + 1) / 2: the next chunk moves up and the one after
       // it is loaded (waited for by the next barrier, used after the one
       // after).
+      if constexpr (T::kFp6) convert_scales6(kt + 1);
       if constexpr (T::kDt == kFp4) {
         convert_scales4<(JB & 1) == 0>(kt + 1);
         if constexpr ((JB & 1) == 0) {
@@ -635,6 +691,8 @@ struct Kernel {
     if constexpr (T::kDt == kFp4)
       acc[I][J] = mma<FIRST && SUB == 0 && H == 0, 2 * SUB + H, H>(f.x[I], f.y[J], acc[I][J], sc_cur[I],
                                                                    sc_cur[4 + J]);
+    else if constexpr (T::kFp6)
+      acc[I][J] = mma<FIRST && SUB == 0, SUB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else if constexpr (T::kScaled)
       acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
@@ -652,7 +710,7 @@ struct Kernel {
   template <int S, int JB, bool FIRST = false>
   __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
     if constexpr (T::kDt == kFp8 && JB == 3) convert_scales((kt + 1) >> 2);
-    if constexpr ((T::kDt == kFp8 && JB == 0 && !FIRST) || (T::kDt == kFp4 && !FIRST)) {
+    if constexpr ((T::kDt == kFp8 && JB == 0 && !FIRST) || ((T::kDt == kFp4 || T::kFp6) && !FIRST)) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
     }
@@ -675,11 +733,11 @@ struct Kernel {
     nk = a.ksteps;
 
     if constexpr (T::kAK)
-      la.init(a.A + (size_t)m0 * a.lda * kElem, min(a.M - m0, TM), K, a.lda, kElem, wave, lane);
+      la.init(a.A + (size_t)m0 * a.lda * kElem, min(a.M - m0, TM), K, a.lda, kElem, kSliceK, wave, lane);
     else
       la.init(a.A, K, a.M, m0, a.lda, wave, lane);
     if constexpr (T::kBK)
-      lb.init(a.B + (size_t)n0 * a.ldb * kElem, min(a.N - n0, TN), K, a.ldb, kElem, wave, lane);
+      lb.init(a.B + (size_t)n0 * a.ldb * kElem, min(a.N - n0, TN), K, a.ldb, kElem, kSliceK, wave, lane);
     else
       lb.init(a.B, K, a.N, n0, a.ldb, wave, lane);
     if constexpr (kPfDist > 0) {
@@ -735,6 +793,8 @@ struct Kernel {
     if constexpr (T::kScaled) {
       if constexpr (T::kDt == kFp8)
         convert_scales(0);
+      else if constexpr (T::kFp6)
+        convert_scales6(0);
       else
         convert_scales4<false>(0);
 #pragma unroll
@@ -948,9 +1008,17 @@ hipError_t launch(const Problem &p) {
     a.ksteps = (a.K + kRowBytes - 1) / kRowBytes;
     a.kb = (int)((p.K + 31) / 32);
   }
+  const bool fp6 = p.dt == Dt::kMxfp6E2M3 || p.dt == Dt::kMxfp6E3M2;
+  if (fp6) {
+    // Rows of bytes (four elements in three), 96-byte slices, a scale per 32.
+    a.K = (int)(p.K / 4 * 3);
+    a.ksteps = (a.K + 95) / 96;
+    a.kb = (int)((p.K + 31) / 32);
+  }
+  const bool scaled = p.dt == Dt::kMxfp8 || p.dt == Dt::kMxfp4 || fp6;
   int tm = p.tile_m, tn = p.tile_n;
   if (tm == 0) {
-    const Shape s = p.dt == Dt::kMxfp8 || p.dt == Dt::kMxfp4 ? Shape{256, 256, 1.0}
+    const Shape s = scaled             ? Shape{256, 256, 1.0}
                     : p.trans_b        ? pick_shape(kShapesBK, p.M, p.N, p.cus)
                                        : pick_shape(kShapesBN, p.M, p.N, p.cus);
     tm = s.tm;
@@ -969,12 +1037,20 @@ hipError_t launch(const Problem &p) {
       if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
         return launch_shape<Traits<kFp4, true, true>, 256, 256>(p, a);
       break;
+    case Dt::kMxfp6E2M3:
+      if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
+        return launch_shape<Traits<kFp6E2M3, true, true>, 256, 256>(p, a);
+      break;
+    case Dt::kMxfp6E3M2:
+      if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
+        return launch_shape<Traits<kFp6E3M2, true, true>, 256, 256>(p, a);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
 bool shape_supported(const Problem &p, int tile_m, int tile_n) {
-  if (p.dt == Dt::kMxfp8 || p.dt == Dt::kMxfp4) return tile_m == 256 && tile_n == 256;
+  if (p.dt != Dt::kBf16 && p.dt != Dt::kF16) return tile_m == 256 && tile_n == 256;
   return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128) ||
          (tile_m == 256 && tile_n == 192 && p.trans_b);
 }

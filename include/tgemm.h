@@ -144,6 +144,42 @@ TGEMM_API int gemm_mxfp4_nt(int64_t M, int64_t N, int64_t K,
                   void *C, hipStream_t stream);
 
 /*
+ * Block-scaled FP6 ("MXFP6") C = (sA * A) . (sB * B)^T, bf16 out.
+ *
+ * Another of the block-scaled formats the Blackwell TCGEN05 GEMM tutorial,
+ * section "进阶" (Advanced), groups with MXFP8; as for MXFP4 the pages fix
+ * no layout, and this follows the OCP MX format: both operands of one OCP
+ * FP6 element type, `fmt`, and one OCP E8M0 scale per 32 consecutive K
+ * elements.  The elements are packed densely: a row of K elements is 3K/4
+ * bytes, element k at bits 6k .. 6k+5 of the row read as a little-endian
+ * bit string (four elements in three bytes).
+ *
+ *   fmt      TGEMM_FP6_E2M3 (0): sign, 2 exponent bits (bias 1), 3 mantissa
+ *            bits, largest value 7.5; TGEMM_FP6_E3M2 (1): sign, 3 exponent
+ *            bits (bias 3), 2 mantissa bits, largest value 28.  No
+ *            infinities or NaN.
+ *   A        device pointer, M x 3K/4 bytes, row-major
+ *   B        device pointer, N x 3K/4 bytes, row-major
+ *   scale_A  device pointer, M x K/32 e8m0 bytes: scale_A[m][j] scales
+ *            A[m][32 j .. 32 j + 31]
+ *   scale_B  device pointer, N x K/32 e8m0 bytes
+ *   C        device pointer, M x N bf16, row-major; written, never read
+ *
+ * C[m][n] is the fp32 sum over k of
+ *   A[m][k] * 2^(scale_A[m][k/32] - 127) * B[n][k] * 2^(scale_B[n][k/32] - 127),
+ * rounded to nearest-even bf16.  K == 0 writes zeros.
+ * Requirements: K % 64 == 0 (whole 16-byte pieces of a row), N % 8 == 0,
+ * A, B and C 16-byte aligned (the scale arrays need no alignment),
+ * 256 * 3K/4 < 2^31.  A fmt other than 0 or 1 returns TGEMM_EINVAL.
+ */
+#define TGEMM_FP6_E2M3 0
+#define TGEMM_FP6_E3M2 1
+TGEMM_API int gemm_mxfp6_nt(int fmt, int64_t M, int64_t N, int64_t K,
+                  const void *A, const void *B,
+                  const void *scale_A, const void *scale_B,
+                  void *C, hipStream_t stream);
+
+/*
  * C = op(A) . op(B) for 16-bit inputs with any operand storage and row
  * strides: bfloat16 in and out (gemm_bf16), fp16 in and out (gemm_f16);
  * fp32 accumulation.
@@ -224,7 +260,7 @@ TGEMM_API const char *tgemm_last_error(void);
  * block_M / block_N; velog "tilelang", 1.1 Front-End DSL).
  *   B stored N x K (gemm_bf16_nt, trans_b = 1): 256x256, 256x192, 128x128
  *   B stored K x N (gemm_f16_nn, trans_b = 0):  256x256, 128x128
- *   gemm_mxfp8_nt, gemm_mxfp4_nt: 256x256
+ *   gemm_mxfp8_nt, gemm_mxfp4_nt, gemm_mxfp6_nt: 256x256
  * Returns TGEMM_OK, or TGEMM_EINVAL for a shape no entry point has; an
  * entry point called with a shape it does not have returns TGEMM_EINVAL.
  * The result does not depend on the tile shape beyond the order of the

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_mxfp4_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
+        ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_mxfp4_nt", "gemm_mxfp6_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
          "tgemm_last_error", "tgemm_set_tile"])
 
 
@@ -64,7 +64,18 @@ def _mx(M, N, K, A=A16, B=B16, SA=0x30000001, SB=0x30800003, C=C16):
     return tg.lib().gemm_mxfp8_nt(M, N, K, A, B, SA, SB, C, None)
 
 
-@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+def _fp4(M, N, K, A=A16, B=B16, SA=0x30000001, SB=0x30800003, C=C16):
+    return tg.lib().gemm_mxfp4_nt(M, N, K, A, B, SA, SB, C, None)
+
+
+def _fp6(M, N, K, A=A16, B=B16, SA=0x30000001, SB=0x30800003, C=C16, fmt=0):
+    return tg.lib().gemm_mxfp6_nt(fmt, M, N, K, A, B, SA, SB, C, None)
+
+
+ALL = [_bf16, _f16, _mx, _fp4, _fp6]
+
+
+@pytest.mark.parametrize("call", ALL)
 def test_empty_outputs_are_a_no_op(call):
     # M == 0 or N == 0: nothing to compute, success without any device work,
     # even with NULL pointers.
@@ -73,14 +84,14 @@ def test_empty_outputs_are_a_no_op(call):
     assert tg.last_error() == ""
 
 
-@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+@pytest.mark.parametrize("call", ALL)
 def test_negative_sizes(call):
     for dims in [(-1, 16, 16), (16, -8, 16), (16, 16, -16)]:
         assert call(*dims) == tg.EINVAL
         assert "negative size" in tg.last_error()
 
 
-@pytest.mark.parametrize("call,kmul", [(_bf16, 8), (_f16, 8), (_mx, 16)])
+@pytest.mark.parametrize("call,kmul", [(_bf16, 8), (_f16, 8), (_mx, 16), (_fp4, 32), (_fp6, 64)])
 def test_vector_width_rules(call, kmul):
     assert call(16, 16, kmul + kmul // 2) == tg.EALIGN
     assert f"multiple of {kmul}" in tg.last_error()
@@ -88,7 +99,7 @@ def test_vector_width_rules(call, kmul):
     assert "N=12 must be a multiple of 8" in tg.last_error()
 
 
-@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+@pytest.mark.parametrize("call", ALL)
 def test_null_and_misaligned_pointers(call):
     assert call(16, 16, 64, A=None) == tg.EINVAL and "A is NULL" in tg.last_error()
     assert call(16, 16, 64, B=None) == tg.EINVAL and "B is NULL" in tg.last_error()
@@ -106,17 +117,24 @@ def test_mxfp8_scale_pointers():
     assert _mx(16, 16, 256, SA=C16 + 100) == tg.EINVAL and "C overlaps scale_A" in tg.last_error()
 
 
-@pytest.mark.parametrize("call", [_bf16, _f16, _mx])
+@pytest.mark.parametrize("call", ALL)
 def test_output_may_not_overlap_inputs(call):
     M, N, K = 64, 64, 64
     assert call(M, N, K, C=A16 + 16) == tg.EINVAL and "C overlaps A" in tg.last_error()
     assert call(M, N, K, C=B16 - 1024 + 16 * 4) == tg.EINVAL and "C overlaps B" in tg.last_error()
 
 
+def test_fp6_format_codes():
+    for bad in (-1, 2, 7):
+        assert _fp6(16, 16, 64, fmt=bad) == tg.EINVAL and "fmt=" in tg.last_error()
+
+
 def test_too_big():
     # 256 rows of a K-slice panel must fit 31-bit buffer offsets.
     assert _bf16(16, 16, 1 << 22) == tg.ETOOBIG and "too large" in tg.last_error()
     assert _mx(16, 16, 1 << 23) == tg.ETOOBIG and "too large" in tg.last_error()
+    assert _fp4(16, 16, 1 << 24) == tg.ETOOBIG and "too large" in tg.last_error()
+    assert _fp6(16, 16, 11 << 20) == tg.ETOOBIG and "too large" in tg.last_error()
     far = 0x7F0000000000     # C far from the (fake, 4 GiB) B
     assert _f16(16, 1 << 16, 1 << 15, C=far) == tg.ETOOBIG and "B too large" in tg.last_error()
     assert _bf16(1 << 31, 16, 16) == tg.ETOOBIG and "below 2^31" in tg.last_error()
