@@ -62,6 +62,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(6))) int i32x6;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -102,6 +103,7 @@ struct Traits {
   static constexpr bool kFp6 = DT == kFp6E2M3 || DT == kFp6E3M2;
   static constexpr int kElem = kScaled ? 1 : 2;
   static constexpr int kSliceBytes = kFp6 ? 96 : 128;  // global bytes of a row per K slice
+  static constexpr int kPitch = kSliceBytes;               // LDS bytes of a slot row
   static constexpr bool kAK = AK, kBK = BK;
 };
 
@@ -210,6 +212,46 @@ struct PanelLoader {
 };
 
 // ---------------------------------------------------------------------------
+// Staging of one K slice of a K-contiguous fp6 panel (96 bytes of each of
+// 64 NI / 6 rows) into a slot of 96-byte rows, packed densely.  Wave w moves
+// 16-byte pieces [64 NI w, 64 NI (w + 1)) of the slot with NI direct-to-LDS
+// instructions; lane l of instruction i writes piece p = 64 (NI w + i) + l,
+// i.e. row p / 6, physical chunk p % 6, and so fetches the logical chunk
+// stored there: a row r keeps logical chunk c at physical chunk
+// (c + rot6(r)) % 6.  With rot6(r) = (r >> 3) & 3 the fragment reads (32
+// rows, one 8-byte piece each) meet at most two to a bank pair, the least
+// that 96-byte rows allow.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int rot6(int r) { return (r >> 3) & 3; }
+
+template <int NI>
+struct DenseLoader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[NI];  // per instruction: byte offset of this lane's chunk at slice 0, or kOOB
+  uint32_t chunks;   // logical chunk of instruction i in bits 3 i .. 3 i + 2
+
+  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int ld, int wave, int lane) {
+    static_assert(3 * NI <= 32, "chunk indices packed in one register");
+    rsrc = make_rsrc(panel, (uint32_t)(rows_valid - 1) * (uint32_t)ld + (uint32_t)K);
+    chunks = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int p = (wave * NI + i) * 64 + lane;
+      const int r = p / 6, c = (p - 6 * r + 6 - rot6(r)) % 6;
+      chunks |= (uint32_t)c << (3 * i);
+      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)ld + 16u * (uint32_t)c : kOOB;
+    }
+  }
+
+  // Instruction i of slice kt; a chunk at or past byte K loads nothing.
+  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k, int i) const {
+    const bool ok = kt * slice_k + 16 * (int)((chunks >> (3 * i)) & 7u) < K;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
+                                             ok ? off[i] : kOOB, (uint32_t)(kt * slice_k), 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Staging of one K slice of an M- or N-contiguous 16-bit operand (A stored
 // K x M, B stored K x N, rows ld elements apart) for a tile of W columns
 // (W = 256 or 128) into a slot of 64 K rows x 2 W bytes.  Wave w moves K
@@ -252,12 +294,13 @@ struct MNLoader {
 // The kernel.
 // ---------------------------------------------------------------------------
 // LDS slots of the K-slice ring.  The 256-row tiles fill the LDS with two
-// (2 x 64 KiB).  A 128 x 128 tile's slice holds a quarter of the MFMA work
+// (2 x 64 KiB); fp6's 96-byte rows leave room for three (3 x 48 KiB),
+// which its short slices (1056 MFMA cycles) need.  A 128 x 128 tile's slice holds a quarter of the MFMA work
 // of a 256 x 256 one, too little to cover the latency of the next slice's
 // loads with one slice in flight, so its ring has four slots (4 x 32 KiB):
 // the loads of slice kt + 4 go out in slice kt, three slices ahead of use.
 template <class T, int TM, int TN>
-constexpr int kSlots = (!T::kScaled && TM * TN <= 128 * 128) ? 4 : 2;
+constexpr int kSlots = T::kFp6 ? 3 : (!T::kScaled && TM * TN <= 128 * 128) ? 4 : 2;
 
 struct Slots {
   LDS_AS uint8_t *a[4];
@@ -270,8 +313,8 @@ struct Kernel {
   static constexpr int kNS = kSlots<T, TM, TN>;
   static constexpr int kElem = T::kElem;
   static constexpr int kWM = TM / 2, kWN = TN / 2;   // wave tile (2 x 2 waves)
-  static constexpr int kSlotA = TM * kRowBytes;      // one slot of A, of B (K-major: 64 K rows x 2 TM / 2 TN bytes)
-  static constexpr int kSlotB = TN * kRowBytes;
+  static constexpr int kSlotA = TM * T::kPitch;      // one slot of A, of B (K-major: 64 K rows x 2 TM / 2 TN bytes)
+  static constexpr int kSlotB = TN * T::kPitch;
   static constexpr int kSliceK = T::kSliceBytes / kElem;  // K elements (packed kinds: bytes) per slice
   // MFMA shape.  16-bit inputs: v_mfma_f32_16x16x32 (it reads and writes 4
   // accumulators per 16 K flops, half the accumulator traffic per flop of
@@ -287,7 +330,9 @@ struct Kernel {
   static constexpr int kHalves = T::kDt == kFp4 ? 2 : 1;
   static constexpr int kPerSub = kNBm * kNBn * kHalves;  // MFMAs per substep
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
-  static constexpr int kLA = TM / 32, kLB = TN / 32;  // load instructions per wave per slice
+  // Load instructions per wave per slice: 8 rows of 128 bytes each, or (fp6)
+  // 64 pieces of 16 bytes of the dense slot.
+  static constexpr int kLA = T::kFp6 ? TM * 6 / 256 : TM / 32, kLB = T::kFp6 ? TN * 6 / 256 : TN / 32;
   static constexpr int kLoads = kLA + kLB;
   static_assert(!T::kScaled || (TM == 256 && TN == 256 && T::kAK && T::kBK),
                 "the block-scaled kernel uses 256 x 256 tiles of K-contiguous operands");
@@ -321,7 +366,8 @@ struct Kernel {
   static constexpr int kLastLoad = kBarrierAt + (kLoads - 1) * kWindow / kLoads;
   static constexpr bool kPfHead = kLastLoad >= kMfma;  // last load in the next slice's head
   static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
-  static constexpr int kPfDist = T::kScaled ? 3 : 0;
+  // (Not for fp6: its three-slot ring already loads slice kt + 3 in slice kt.)
+  static constexpr int kPfDist = T::kScaled && !T::kFp6 ? 3 : 0;
   static_assert(!kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
   static_assert(kPfHead || kPfAt < kMfma, "prefetch position");
 
@@ -345,7 +391,8 @@ struct Kernel {
     return -1;
   }
 
-  using Frag = typename std::conditional<kW, i32x8, u32x4>::type;
+  // fp6 fragments are 24 bytes: six registers.
+  using Frag = typename std::conditional<T::kFp6, i32x6, typename std::conditional<kW, i32x8, u32x4>::type>::type;
   using Acc = typename std::conditional<kW, f32x16, f32x4>::type;
   struct Frags {
     Frag x[kNBn], y[kNBm];
@@ -356,8 +403,11 @@ struct Kernel {
   int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
-  typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type la;
-  typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type lb;
+  typename std::conditional<T::kFp6, DenseLoader<kLA>,
+                            typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type>::type la;
+  typename std::conditional<T::kFp6, DenseLoader<kLB>,
+                            typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type>::type lb;
+  int f6off[6];  // fp6: byte offset of this lane's 8-byte pieces (K step s, piece q at 3 s + q) in a block
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
   // Block scales.  Each lane streams the scale bytes of one row per
@@ -394,15 +444,13 @@ struct Kernel {
   __device__ __forceinline__ Frag read_rows(const LDS_AS uint8_t *slot, int row0, int sub) const {
     if constexpr (T::kFp6) {
       // 32 x 32 x 64 on fp6: lane l holds row l % 32 and 24 bytes (32
-      // elements) of K: bytes 48 sub + 24 (l / 32) .. + 23, read as three
-      // 8-byte pieces (a 16-byte chunk holds two).  Registers 6 and 7 are
-      // not used by the MFMA.
-      const LDS_AS uint8_t *p = slot + (row0 + (lane & 31)) * kRowBytes;
-      i32x8 r = {};
+      // elements) of K: bytes 48 sub + 24 (l / 32) .. + 23, three 8-byte
+      // pieces at the offsets set up in run().
+      const LDS_AS uint8_t *p = slot + row0 * T::kPitch;
+      i32x6 r;
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
-        const int b = 48 * sub + 24 * (lane >> 5) + 8 * q;
-        const u32x2 v = *(const LDS_AS u32x2 *)(p + ((((b >> 4) ^ lane_sw) << 4) | (b & 8)));
+        const u32x2 v = *(const LDS_AS u32x2 *)(p + f6off[3 * sub + q]);
         r[2 * q] = (int)v[0];
         r[2 * q + 1] = (int)v[1];
       }
@@ -571,10 +619,12 @@ struct Kernel {
   // Chunk c of every instruction's row into dst.  The resource ends at the
   // dword holding the tile's last scale byte; the hardware checks each dword
   // of the load against it (soffset included), so dwords past it read 0.
-  __device__ __forceinline__ void load_chunks(u32x4 (&dst)[4], int c) {
+  __device__ __forceinline__ void load_chunks(u32x4 (&dst)[4], int c) { load_bytes16(dst, 16 * c); }
+  // The 16 bytes from byte b (a multiple of 4) of every instruction's row.
+  __device__ __forceinline__ void load_bytes16(u32x4 (&dst)[4], int b) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rss[j >> 1], sc_off[j], 16u * (uint32_t)c, 0);
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rss[j >> 1], sc_off[j], (uint32_t)b, 0);
   }
 
   // Mask keeping the bytes of a dword that holds scale blocks b .. b + 3 of
@@ -626,26 +676,31 @@ struct Kernel {
     if ((g & 3) == 3) load_chunks(sc_ckn, (g >> 2) + 2);
   }
 
-  // fp6: slice t's 4 scale bytes per row (groups 0-3 of its 128 elements),
-  // shifted out of the window's first two dwords; the MFMA of K step s, in
-  // wave half w, uses group 2 s + w, so lanes 0-31 take groups 0, 2 and
-  // lanes 32-63 groups 1, 3, in byte s.  The window then moves on by one
-  // dword; once it has moved a whole chunk the chunk after the next is
-  // loaded (waited for by the next barrier, used after it).
+  // fp6: slice t's 4 scale bytes per row (groups 0-3 of its 128 elements).
+  // Its chunks are 16 bytes every 12 (slices 3 c .. 3 c + 2 and the bytes
+  // an unaligned row start shifts in), so slice t = 3 c + POS is dwords POS
+  // and POS + 1 of chunk c: with slice kt in slot kt % 3, POS is fixed for
+  // every step, and no index is dynamic.  The MFMA of K step s in wave half
+  // w uses group 2 s + w, so lanes 0-31 take groups 0, 2 and lanes 32-63
+  // groups 1, 3, in byte s.  After a chunk's last slice the next chunk
+  // moves up and the one after it is loaded (three slices ahead of use).
+  template <int POS>
   __device__ __forceinline__ void convert_scales6(int t) {
     const uint32_t keep = keep_mask(a.kb - 4 * t);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t d = __builtin_amdgcn_alignbyte(sc_ck[j][1], sc_ck[j][0], sc_sh[j]) & keep;
+      const uint32_t d = __builtin_amdgcn_alignbyte(sc_ck[j][POS + 1], sc_ck[j][POS], sc_sh[j]) & keep;
       const uint32_t lo = __builtin_amdgcn_perm(0u, d, 0x0c0c0200u);  // groups 0, 2
       const uint32_t hi = __builtin_amdgcn_perm(0u, d, 0x0c0c0301u);  // groups 1, 3
       const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
       sc_nxt[2 * j] = (int)sw[0];
       sc_nxt[2 * j + 1] = (int)sw[1];
-      sc_ck[j] = u32x4{sc_ck[j][1], sc_ck[j][2], sc_ck[j][3], sc_ckn[j][0]};
-      sc_ckn[j] = u32x4{sc_ckn[j][1], sc_ckn[j][2], sc_ckn[j][3], 0u};
     }
-    if ((t & 3) == 3) load_chunks(sc_ckn, (t >> 2) + 2);
+    if constexpr (POS == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc_ck[j] = sc_ckn[j];
+      load_bytes16(sc_ckn, 12 * (t / 3 + 2));
+    }
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
@@ -672,7 +727,7 @@ struct Kernel {
       // ends chunk (kt + 1) / 2: the next chunk moves up and the one after
       // it is loaded (waited for by the next barrier, used after the one
       // after).
-      if constexpr (T::kFp6) convert_scales6(kt + 1);
+      if constexpr (T::kFp6) convert_scales6<(S + 1) % 3>(kt + 1);
       if constexpr (T::kDt == kFp4) {
         convert_scales4<(JB & 1) == 0>(kt + 1);
         if constexpr ((JB & 1) == 0) {
@@ -732,14 +787,28 @@ struct Kernel {
     const int K = a.K;
     nk = a.ksteps;
 
-    if constexpr (T::kAK)
+    if constexpr (T::kFp6)
+      la.init(a.A + (size_t)m0 * a.lda, min(a.M - m0, TM), K, a.lda, wave, lane);
+    else if constexpr (T::kAK)
       la.init(a.A + (size_t)m0 * a.lda * kElem, min(a.M - m0, TM), K, a.lda, kElem, kSliceK, wave, lane);
     else
       la.init(a.A, K, a.M, m0, a.lda, wave, lane);
-    if constexpr (T::kBK)
+    if constexpr (T::kFp6)
+      lb.init(a.B + (size_t)n0 * a.ldb, min(a.N - n0, TN), K, a.ldb, wave, lane);
+    else if constexpr (T::kBK)
       lb.init(a.B + (size_t)n0 * a.ldb * kElem, min(a.N - n0, TN), K, a.ldb, kElem, kSliceK, wave, lane);
     else
       lb.init(a.B, K, a.N, n0, a.ldb, wave, lane);
+    if constexpr (T::kFp6) {
+      // Fragment rows start at multiples of 32, so a lane's row has rot6 of
+      // lane % 32.  Logical 8-byte piece 6 s + 3 (l / 32) + q of the row.
+#pragma unroll
+      for (int sq = 0; sq < 6; ++sq) {
+        const int u = 6 * (sq / 3) + 3 * (lane >> 5) + sq % 3;
+        const int c = ((u >> 1) + rot6(lane & 31)) % 6;
+        f6off[sq] = (lane & 31) * T::kPitch + 16 * c + 8 * (u & 1);
+      }
+    }
     if constexpr (kPfDist > 0) {
       // Waves 0-1 take 32 rows of the A panel (its share among the 8 tile
       // columns of an XCD's block), waves 2-3 take 64 rows of the B panel
@@ -781,7 +850,10 @@ struct Kernel {
     // of slice 1 that a previous slice's tail would have issued; wait for
     // all but those, and convert slice 0's scales.  (With K = 0 every slice
     // is all zeros.)
-    if constexpr (T::kScaled) {
+    if constexpr (T::kFp6) {
+      load_bytes16(sc_ck, 0);
+      load_bytes16(sc_ckn, 12);
+    } else if constexpr (T::kScaled) {
       load_chunks(sc_ck, 0);
       load_chunks(sc_ckn, 1);
     }
@@ -794,7 +866,7 @@ struct Kernel {
       if constexpr (T::kDt == kFp8)
         convert_scales(0);
       else if constexpr (T::kFp6)
-        convert_scales6(0);
+        convert_scales6<0>(0);
       else
         convert_scales4<false>(0);
 #pragma unroll
@@ -815,6 +887,15 @@ struct Kernel {
         step<1, 3>(kt + 2, f0, f1);
         step<0, 0>(kt + 3, f0, f1);
       }
+    } else if constexpr (kNS == 3) {
+      int kt = 1;
+      for (; kt + 2 < nk; kt += 3) {
+        step<1, 1>(kt, f0, f1);
+        step<2, 2>(kt + 1, f0, f1);
+        step<0, 0>(kt + 2, f0, f1);
+      }
+      if (kt < nk) step<1, 1>(kt, f0, f1);
+      if (kt + 1 < nk) step<2, 2>(kt + 1, f0, f1);
     } else if constexpr (kNS == 4) {
       // Four at a time, then the one to three left (no padding: a padded
       // slice is a quarter of a short K's work).
@@ -888,16 +969,22 @@ void gemm_kernel(const Args a) {
   // A separate array per slot (not one indexed array) so the compiler can
   // tell the slot being loaded from the slot being read and does not insert
   // a vmcnt wait in front of every LDS read.
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TM * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[TM * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[TN * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[TN * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TM * T::kPitch];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[TM * T::kPitch];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[TN * T::kPitch];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[TN * T::kPitch];
   __shared__ __attribute__((aligned(256))) uint8_t junk[4 * 256];
   Slots slots;
   slots.a[0] = (LDS_AS uint8_t *)sA0;
   slots.a[1] = (LDS_AS uint8_t *)sA1;
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
+  if constexpr (kSlots<T, TM, TN> == 3) {
+    __shared__ __attribute__((aligned(1024))) uint8_t sA2[TM * T::kPitch];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB2[TN * T::kPitch];
+    slots.a[2] = (LDS_AS uint8_t *)sA2;
+    slots.b[2] = (LDS_AS uint8_t *)sB2;
+  }
   if constexpr (kSlots<T, TM, TN> == 4) {
     __shared__ __attribute__((aligned(1024))) uint8_t sA2[TM * kRowBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t sA3[TM * kRowBytes];
