@@ -875,18 +875,22 @@ struct Kernel {
     barrier();
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
-    // Slice 0 starts the accumulators; then slices go two (fp8: four) at a
-    // time, alternating slots.  The count is padded: a slice past nk
-    // arrives as zeros and adds nothing.  (Leaving the loop early instead
-    // makes the register allocator copy the accumulators around and spill.)
+    // Slice 0 starts the accumulators; then the slices go round the ring a
+    // whole number of slots at a time (fp8: four, for its scale groups),
+    // and the one to three left after the last round run on their own, so
+    // no slice past nk is computed.
     step<0, 0, true>(0, f0, f1);
     if constexpr (T::kDt == kFp8) {
-      for (int kt = 1; kt < nk; kt += 4) {
+      int kt = 1;
+      for (; kt + 3 < nk; kt += 4) {
         step<1, 1>(kt, f0, f1);
         step<0, 2>(kt + 1, f0, f1);
         step<1, 3>(kt + 2, f0, f1);
         step<0, 0>(kt + 3, f0, f1);
       }
+      if (kt < nk) step<1, 1>(kt, f0, f1);
+      if (kt + 1 < nk) step<0, 2>(kt + 1, f0, f1);
+      if (kt + 2 < nk) step<1, 3>(kt + 2, f0, f1);
     } else if constexpr (kNS == 3) {
       int kt = 1;
       for (; kt + 2 < nk; kt += 3) {
@@ -897,8 +901,6 @@ struct Kernel {
       if (kt < nk) step<1, 1>(kt, f0, f1);
       if (kt + 1 < nk) step<2, 2>(kt + 1, f0, f1);
     } else if constexpr (kNS == 4) {
-      // Four at a time, then the one to three left (no padding: a padded
-      // slice is a quarter of a short K's work).
       int kt = 1;
       for (; kt + 3 < nk; kt += 4) {
         step<1, 1>(kt, f0, f1);
@@ -910,10 +912,12 @@ struct Kernel {
       if (kt + 1 < nk) step<2, 2>(kt + 1, f0, f1);
       if (kt + 2 < nk) step<3, 3>(kt + 2, f0, f1);
     } else {
-      for (int kt = 1; kt < nk; kt += 2) {
+      int kt = 1;
+      for (; kt + 1 < nk; kt += 2) {
         step<1, 1>(kt, f0, f1);
         step<0, 2>(kt + 1, f0, f1);
       }
+      if (kt < nk) step<1, 1>(kt, f0, f1);
     }
     // Drain the loads still in flight into the slots before the workgroup
     // can finish.
