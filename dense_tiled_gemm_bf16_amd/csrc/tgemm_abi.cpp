@@ -276,8 +276,9 @@ int quantize_mxfp8(int64_t M, int64_t K, const float *x, void *q, void *scales, 
 int tgemm_set_tile(int tile_m, int tile_n) {
   g_err[0] = '\0';
   const bool known = (tile_m == 0 && tile_n == 0) || (tile_m == 256 && tile_n == 256) ||
-                     (tile_m == 256 && tile_n == 192) || (tile_m == 128 && tile_n == 128);
-  if (!known) return fail(TGEMM_EINVAL, "tgemm_set_tile: no %dx%d tile (256x256, 256x192, 128x128 or 0x0)", tile_m, tile_n);
+                     (tile_m == 256 && tile_n == 192) || (tile_m == 128 && tile_n == 128) ||
+                     (tile_m == 64 && tile_n == 64);
+  if (!known) return fail(TGEMM_EINVAL, "tgemm_set_tile: no %dx%d tile (256x256, 256x192, 128x128, 64x64 or 0x0)", tile_m, tile_n);
   g_tile_m = tile_m;
   g_tile_n = tile_n;
   return TGEMM_OK;

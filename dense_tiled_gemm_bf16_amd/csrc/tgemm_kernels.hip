@@ -145,10 +145,20 @@ __device__ __forceinline__ void barrier() {
 // (r & 7) ^ ((r >> 3) & 1) conflicts 2-way on the 16 x 16 pattern.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// NN B slot: 64 K rows of 512 bytes (256 columns).  Row k keeps logical
-// chunk c at physical chunk c ^ swz_nn(k); measured conflict-free for the
-// transpose reads, which take four consecutive K rows at a time.
-__device__ __forceinline__ int swz_nn(int k) { return ((k & 3) << 2) ^ ((k >> 2) & 3); }
+// K-major slot of W columns: 64 K rows of 2 W bytes.  Row k keeps logical
+// chunk c at physical chunk c ^ swz_nn<W>(k).  For W = 256 and 128 the
+// permutation was measured conflict-free for the transpose reads, which take
+// four consecutive K rows at a time.  A 128-byte row (W = 64) has only 8
+// chunks; there the reads' 32-byte column segments move by whole segments,
+// so that the 8 K rows a half-wave reads (8 g + 4 t + e, g < 2, e < 4) fall
+// on 8 different 32-byte bank groups.
+template <int W>
+__device__ __forceinline__ int swz_nn(int k) {
+  if constexpr (W == 64)
+    return (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1;
+  else
+    return ((k & 3) << 2) ^ ((k >> 2) & 3);
+}
 
 // Workgroup id -> output tile.  Consecutive workgroup ids are placed on the
 // 8 XCDs in turn; renumber so that the ids sharing an XCD are consecutive,
@@ -262,7 +272,7 @@ struct DenseLoader {
 // ---------------------------------------------------------------------------
 template <int W>
 struct MNLoader {
-  static_assert(W == 256 || W == 128, "an instruction covers whole K rows of the slot");
+  static_assert(W == 256 || W == 128 || W == 64, "an instruction covers whole K rows of the slot");
   static constexpr int NI = W / 32, RPI = 512 / W, LPR = W / 8;
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t off[NI];  // per instruction: byte offset at slice 0 (kOOB past the last column)
@@ -278,7 +288,7 @@ struct MNLoader {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int kr = krow0 + RPI * i;
-      const int c = c0 + ((lane % LPR) ^ swz_nn(kr)) * 8;
+      const int c = c0 + ((lane % LPR) ^ swz_nn<W>(kr)) * 8;
       off[i] = c < ext ? (uint32_t)kr * row_bytes + (uint32_t)c * 2u : kOOB;
     }
   }
@@ -368,8 +378,8 @@ struct Kernel {
   static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
   // (Not for fp6: its three-slot ring already loads slice kt + 3 in slice kt.)
   static constexpr int kPfDist = T::kScaled && !T::kFp6 ? 3 : 0;
-  static_assert(!kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
-  static_assert(kPfHead || kPfAt < kMfma, "prefetch position");
+  static_assert(kPfDist == 0 || !kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
+  static_assert(kPfDist == 0 || kPfHead || kPfAt < kMfma, "prefetch position");
 
   // Loads of a slice issued in the tail of the slice kNS before it.
   static constexpr int tail_loads() {
@@ -490,7 +500,7 @@ struct Kernel {
       const int kr = 32 * sub + 8 * g + 4 * t + e;
       // (Masked to the slot so the compiler can see the read stays inside it
       // and needs no wait for loads into the other slot.)
-      const int off = (kr * (2 * W) + (((n >> 3) ^ swz_nn(kr)) << 4) + (n & 7) * 2) & (W * kRowBytes - 1);
+      const int off = (kr * (2 * W) + (((n >> 3) ^ swz_nn<W>(kr)) << 4) + (n & 7) * 2) & (W * kRowBytes - 1);
       const LDS_AS uint8_t *p = slot + off;
       s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)p);
       u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -1023,6 +1033,7 @@ hipError_t launch_layout(const Problem &p, const Args &a, int tm, int tn) {
   if constexpr (BK)
     if (tm == 256 && tn == 192) return launch_shape<T, 256, 192>(p, a);
   if (tm == 128 && tn == 128) return launch_shape<T, 128, 128>(p, a);
+  if (tm == 64 && tn == 64) return launch_shape<T, 64, 64>(p, a);
   return hipErrorInvalidValue;
 }
 
@@ -1039,21 +1050,26 @@ hipError_t launch_dt(const Problem &p, const Args &a, int tm, int tn) {
 // 256 x 256 per unit of tile area in a wave of workgroups (one workgroup
 // per CU).  The rates are fitted to sustained measurements on MI355X
 // (bf16 NT unless noted, us):
-//                        256x256  256x192  128x128
-//   4096 x 4096 x 8192     193      --       251    (rate 0.77 here)
-//   3072 x 3072 x 3072      65      --        74
-//   4000 x 3000 x 5000     118     117       156
-//   2048 x 2048 x 4096      78      63        35
-//   2048 x 1024 x 4096      77      --        27
-//   fp16 NN 1024^3          31      --        11.8
+//                        256x256  256x192  128x128  64x64
+//   4096 x 4096 x 8192     193      --       251      --   (rate 0.77 here)
+//   3072 x 3072 x 3072      65      --        74      --
+//   4000 x 3000 x 5000     118     117       156      --
+//   2048 x 2048 x 4096      78      63        35      --
+//   2048 x 1024 x 4096      77      --        27      --
+//   512 x 512 x 4096        --      --        25.8    12.2
+//   fp16 NN 2048 x 1024^2   --      --        12.0    11.1
+//   fp16 NN 1024^3          31      --        11.8     6.2
+//   256^3                   --      --         5.9     3.7
 // 0.70 for 128 x 128 sits between the first two rows: a partly filled last
-// wave runs at a higher clock under the power cap than whole ones.
+// wave runs at a higher clock under the power cap than whole ones.  0.35
+// for 64 x 64 fits the rows below it, where a slice's loads and barrier,
+// not its 8 MFMAs per wave, set the pace.
 struct Shape {
   int tm, tn;
   double rel;
 };
-constexpr Shape kShapesBK[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.70}};  // B K-contiguous
-constexpr Shape kShapesBN[] = {{256, 256, 1.0}, {128, 128, 0.70}};                     // B N-contiguous
+constexpr Shape kShapesBK[] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.70}, {64, 64, 0.35}};  // B K-contiguous
+constexpr Shape kShapesBN[] = {{256, 256, 1.0}, {128, 128, 0.70}, {64, 64, 0.35}};                     // B N-contiguous
 
 // The shape with the least estimated time: whole waves of tiles over the
 // CUs, each wave costing its tile area over the shape's relative rate.
@@ -1142,7 +1158,7 @@ hipError_t launch(const Problem &p) {
 
 bool shape_supported(const Problem &p, int tile_m, int tile_n) {
   if (p.dt != Dt::kBf16 && p.dt != Dt::kF16) return tile_m == 256 && tile_n == 256;
-  return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128) ||
+  return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128) || (tile_m == 64 && tile_n == 64) ||
          (tile_m == 256 && tile_n == 192 && p.trans_b);
 }
 

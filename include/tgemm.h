@@ -258,8 +258,8 @@ TGEMM_API const char *tgemm_last_error(void);
  * fewest waves of workgroups for the least work (the pages' kernels take
  * their block sizes as parameters: SM100 README, "Code Example",
  * block_M / block_N; velog "tilelang", 1.1 Front-End DSL).
- *   B stored N x K (gemm_bf16_nt, trans_b = 1): 256x256, 256x192, 128x128
- *   B stored K x N (gemm_f16_nn, trans_b = 0):  256x256, 128x128
+ *   B stored N x K (gemm_bf16_nt, trans_b = 1): 256x256, 256x192, 128x128, 64x64
+ *   B stored K x N (gemm_f16_nn, trans_b = 0):  256x256, 128x128, 64x64
  *   gemm_mxfp8_nt, gemm_mxfp4_nt, gemm_mxfp6_nt: 256x256
  * Returns TGEMM_OK, or TGEMM_EINVAL for a shape no entry point has; an
  * entry point called with a shape it does not have returns TGEMM_EINVAL.

@@ -164,7 +164,7 @@ def test_set_tile_validates_shapes():
     assert L.tgemm_set_tile(100, 100) == tg.EINVAL
     assert "no 100x100 tile" in tg.last_error()
     assert L.tgemm_set_tile(256, 128) == tg.EINVAL
-    for tm, tn in [(256, 256), (256, 192), (128, 128), (0, 0)]:
+    for tm, tn in [(256, 256), (256, 192), (128, 128), (64, 64), (0, 0)]:
         assert L.tgemm_set_tile(tm, tn) == tg.OK
         assert tg.last_error() == ""
 

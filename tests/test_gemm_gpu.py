@@ -268,8 +268,8 @@ def test_mid_size_full_parity_several_tiles(kind):
 
 # --- every tile shape, forced ----------------------------------------------------------
 
-SHAPES = [("bf16_nt", 256, 256), ("bf16_nt", 256, 192), ("bf16_nt", 128, 128),
-          ("f16_nn", 256, 256), ("f16_nn", 128, 128), ("mxfp8_nt", 256, 256)]
+SHAPES = [("bf16_nt", 256, 256), ("bf16_nt", 256, 192), ("bf16_nt", 128, 128), ("bf16_nt", 64, 64),
+          ("f16_nn", 256, 256), ("f16_nn", 128, 128), ("f16_nn", 64, 64), ("mxfp8_nt", 256, 256)]
 
 
 @pytest.fixture

@@ -96,7 +96,7 @@ LAYOUTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
 
 
 def shapes_for(tb):
-    return [(256, 256), (128, 128)] + ([(256, 192)] if tb else [])
+    return [(256, 256), (128, 128), (64, 64)] + ([(256, 192)] if tb else [])
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
