@@ -940,38 +940,70 @@ struct Kernel {
   // (C rows) m0 + kWM wave_m + kBlk j.  32 x 32 blocks: lane l, register r
   // holds C row l % 32 of the block, column 8 (r / 4) + 4 (l / 32) + r % 4.
   // 16 x 16 blocks: lane l, register r holds row l % 16, column
-  // 4 (l / 16) + r.  Either way four consecutive columns leave as one
-  // 8-byte store.
+  // 4 (l / 16) + r.
+  //
+  // Four fp32 -> one 8-byte group of C values (bf16, or fp16 for fp16 inputs).
+  __device__ __forceinline__ u32x2 pack4(const Acc &c, int r0) const {
+    const f32x2 lo = {c[r0], c[r0 + 1]};
+    const f32x2 up = {c[r0 + 2], c[r0 + 3]};
+    u32x2 pk;
+    if constexpr (T::kDt == kF16) {
+      pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2));
+      pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(up, f16x2));
+    } else {
+      pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+      pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(up, bf16x2));
+    }
+    return pk;
+  }
+
   __device__ __forceinline__ void epilogue() {
-    constexpr int kGroups = kBlk == 32 ? 4 : 1;
     const int row_l = lane % kBlk;
-    const int colq = kBlk == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
+    if constexpr (kBlk == 32) {
+      // 32 x 32 blocks: lanes l and l + 32 hold the same row, columns
+      // 8 g .. 8 g + 3 and 8 g + 4 .. 8 g + 7 of group g.  One swap of the
+      // wave halves per pair of groups (2 p, 2 p + 1) gives lane l columns
+      // 16 p .. 16 p + 7 and lane l + 32 columns 16 p + 8 .. 16 p + 15, so
+      // each lane leaves 16 bytes per store and a store instruction writes
+      // 32 contiguous bytes of each of 32 rows.  (Every lane swaps; only the
+      // stores are masked.)
+      const int half = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < kNBm; ++j) {
-      const int m = m0 + wave_m * kWM + j * kBlk + row_l;
-      if (m >= a.M) continue;
-      uint8_t *crow = a.C + (size_t)m * a.ldc * 2;
+      for (int j = 0; j < kNBm; ++j) {
+        const int m = m0 + wave_m * kWM + j * kBlk + row_l;
+        uint8_t *crow = a.C + (size_t)m * a.ldc * 2;
 #pragma unroll
-      for (int i = 0; i < kNBn; ++i) {
+        for (int i = 0; i < kNBn; ++i) {
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          const int n = n0 + wave_n * kWN + i * kBlk + g * 8 + colq;
-          if (n >= a.N) continue;
-          const f32x2 lo = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]};
-          const f32x2 up = {acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          u32x2 pk;
-          if constexpr (T::kDt == kF16) {
-            pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2));
-            pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(up, f16x2));
-          } else {
-            pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-            pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(up, bf16x2));
+          for (int pr = 0; pr < 2; ++pr) {
+            const u32x2 p0 = pack4(acc[i][j], 8 * pr), p1 = pack4(acc[i][j], 8 * pr + 4);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(p0[0], p1[0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(p0[1], p1[1], false, false);
+            const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+            const int n = n0 + wave_n * kWN + i * kBlk + 16 * pr + 8 * half;
+            if (m < a.M && n < a.N) *(u32x4 *)(crow + (size_t)n * 2) = out;
           }
-          *(u32x2 *)(crow + (size_t)n * 2) = pk;
+        }
+      }
+    } else {
+      // 16 x 16 blocks: lane l, register r holds row l % 16, column
+      // 4 (l / 16) + r; one 8-byte store per block.
+      const int colq = 4 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < kNBm; ++j) {
+        const int m = m0 + wave_m * kWM + j * kBlk + row_l;
+        if (m >= a.M) continue;
+        uint8_t *crow = a.C + (size_t)m * a.ldc * 2;
+#pragma unroll
+        for (int i = 0; i < kNBn; ++i) {
+          const int n = n0 + wave_n * kWN + i * kBlk + colq;
+          if (n >= a.N) continue;
+          *(u32x2 *)(crow + (size_t)n * 2) = pack4(acc[i][j], 0);
         }
       }
     }
   }
+
 };
 
 // One workgroup per CU: either shape's ring takes 128 KiB of the 160 KiB
