@@ -986,19 +986,34 @@ struct Kernel {
         }
       }
     } else {
-      // 16 x 16 blocks: lane l, register r holds row l % 16, column
-      // 4 (l / 16) + r; one 8-byte store per block.
-      const int colq = 4 * (lane >> 4);
+      // 16 x 16 blocks: lane l holds row l % 16, columns 4 (l / 16) .. + 3.
+      // Per pair of blocks (i, i + 1) the 16-lane rows q of the wave hold
+      // X_q = columns 4 q .. of block i and Y_q of block i + 1.  A swap of
+      // the wave halves, then of odd and even 16-lane rows, leaves row q
+      // with columns 8 q .. 8 q + 7 of the 32 (X_0 X_1 | X_2 X_3 | Y_0 Y_1 |
+      // Y_2 Y_3), so each lane stores 16 bytes and an instruction writes 64
+      // contiguous bytes of each of 16 rows.  (The lanes that trade hold the
+      // same row, so a row's lanes are all in or all out of range.)
+      static_assert(kNBn % 2 == 0, "blocks pair up along N");
+      const int q = lane >> 4;
 #pragma unroll
       for (int j = 0; j < kNBm; ++j) {
         const int m = m0 + wave_m * kWM + j * kBlk + row_l;
-        if (m >= a.M) continue;
         uint8_t *crow = a.C + (size_t)m * a.ldc * 2;
 #pragma unroll
-        for (int i = 0; i < kNBn; ++i) {
-          const int n = n0 + wave_n * kWN + i * kBlk + colq;
-          if (n >= a.N) continue;
-          *(u32x2 *)(crow + (size_t)n * 2) = pack4(acc[i][j], 0);
+        for (int i = 0; i < kNBn; i += 2) {
+          const u32x2 x = pack4(acc[i][j], 0), y = pack4(acc[i + 1][j], 0);
+          uint32_t xo[2], yo[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const auto h = __builtin_amdgcn_permlane32_swap(x[d], y[d], false, false);
+            const auto r = __builtin_amdgcn_permlane16_swap(h[0], h[1], false, false);
+            xo[d] = r[0];
+            yo[d] = r[1];
+          }
+          const u32x4 out = {xo[0], xo[1], yo[0], yo[1]};
+          const int n = n0 + wave_n * kWN + i * kBlk + 8 * q;
+          if (m < a.M && n < a.N) *(u32x4 *)(crow + (size_t)n * 2) = out;
         }
       }
     }
