@@ -354,9 +354,12 @@ struct Kernel {
   // too short a window overrun the texture unit (about 64 bytes per clock
   // per CU) and stall the MFMA stream behind a full queue.  The barrier
   // positions are the measured best (fewest cycles per workgroup): halfway
-  // for the 128-MFMA 16-bit slice, three quarters for the 32-MFMA fp8 slice.
-  static constexpr int kBarrierAt = T::kScaled ? kMfma * 3 / 4 : kMfma / 2;
-  static constexpr int kWindow = kMfma / 2;
+  // for the 128-MFMA 16-bit slice, three quarters for the 32-MFMA fp8 slice;
+  // halfway with loads spread over three quarters of a slice for fp4 and
+  // fp6 (about 3% fewer cycles than three quarters and a half).
+  static constexpr bool kFp46 = T::kDt == kFp4 || T::kFp6;
+  static constexpr int kBarrierAt = T::kDt == kFp8 ? kMfma * 3 / 4 : kMfma / 2;
+  static constexpr int kWindow = kFp46 ? kMfma * 3 / 4 : kMfma / 2;
   static_assert(kBarrierAt + kNR <= kMfma, "next-slice fragment reads must fit after the barrier");
   static_assert(kNR <= kBarrierAt, "this slice's second-substep reads come before the barrier");
   static_assert(kWindow <= kMfma && kWindow >= kLoads, "load window");
