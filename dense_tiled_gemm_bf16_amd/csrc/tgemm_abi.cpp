@@ -79,6 +79,10 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 
 constexpr uint64_t kOffsetLimit = 0x7fffffffull;  // the kernels use 31-bit buffer offsets
 
+// Bytes spanned by the K rows of a K-major 16-bit operand with row stride ld,
+// K rounded up to whole slices of 64 rows.
+uint64_t k_rows_bytes(int64_t K, int64_t ld) { return (uint64_t)(K + 63) / 64 * 64 * (uint64_t)ld * 2; }
+
 struct Operand {
   const char *name;
   const void *ptr;
@@ -172,9 +176,10 @@ int gemm_general(const char *fn, tgemm::Dt dt, int trans_a, int trans_b, int64_t
     if (overlaps(C, c_bytes, o.ptr, o.bytes)) return fail(TGEMM_EINVAL, "%s: C overlaps %s", fn, o.name);
   }
   // 31-bit buffer offsets: a K-contiguous operand is addressed per panel of
-  // 256 rows, an M/N-contiguous one as a whole.
-  const uint64_t a_span = trans_a ? a_bytes : (uint64_t)tgemm::kTileM * lda * 2;
-  const uint64_t b_span = trans_b ? (uint64_t)tgemm::kTileN * ldb * 2 : b_bytes;
+  // 256 rows, an M/N-contiguous one as a whole, in whole slices of 64 K rows
+  // (the ragged last slice reads its rows past K as out of range).
+  const uint64_t a_span = trans_a ? k_rows_bytes(K, lda) : (uint64_t)tgemm::kTileM * lda * 2;
+  const uint64_t b_span = trans_b ? (uint64_t)tgemm::kTileN * ldb * 2 : k_rows_bytes(K, ldb);
   if (a_span > kOffsetLimit) return fail(TGEMM_ETOOBIG, "%s: A too large for 31-bit offsets", fn);
   if (b_span > kOffsetLimit) return fail(TGEMM_ETOOBIG, "%s: B too large for 31-bit offsets", fn);
   tgemm::Problem p{dt, trans_a == 1, trans_b == 1, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream,
@@ -306,8 +311,8 @@ int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, v
   if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
   if ((uint64_t)tgemm::kTileM * k * 2 > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
-  if (k * n * 2 > kOffsetLimit)
-    return fail(TGEMM_ETOOBIG, "%s: B too large (K * N * 2 bytes must stay below 2^31)", fn);
+  if (k_rows_bytes(K, N) > kOffsetLimit)
+    return fail(TGEMM_ETOOBIG, "%s: B too large (K * N * 2 bytes, K rounded up to 64, must stay below 2^31)", fn);
   tgemm::Problem p{tgemm::Dt::kF16, false, false, M, N, K, A, K, B, N, nullptr, nullptr, C, N, stream, 0, 0, 0};
   return dispatch(fn, p);
 }

@@ -212,12 +212,34 @@ struct PanelLoader {
     }
   }
 
-  // Instruction i of slice kt.  A chunk at or past column K (the ragged last
-  // slice, or a slice past the end) takes an out-of-range offset.
-  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k, int i) const {
+  // Instruction i of slice kt.  Columns are not checked: in the ragged last
+  // slice a chunk at or past column K reads the start of the next row (past
+  // the panel's last row, zeros from the range check), and zero_tail()
+  // clears it once it has landed; slices past the last one land in slots
+  // that are never read.  (A per-load select right before each load stalled
+  // the MFMA stream: 8% more cycles per workgroup.)
+  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int i) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16, off[i],
+                                             (uint32_t)kt * slice_bytes, 0, 0);
+  }
+
+  // The same with the column check: a chunk at or past column K takes an
+  // out-of-range offset (the MXFP8 kernel, which a zeroing branch inside its
+  // slice would push into spilling registers).
+  __device__ __forceinline__ void issue_masked(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k,
+                                               int i) const {
     const bool ok = kt * slice_k + kcol[i & 1] < K;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
                                              ok ? off[i] : kOOB, (uint32_t)kt * slice_bytes, 0, 0);
+  }
+
+  // Zero the chunks this lane loaded for slice kt (in `slot`) that lie at or
+  // past column K.
+  __device__ __forceinline__ void zero_tail(LDS_AS uint8_t *slot, int wave, int lane, int kt, int K,
+                                            int slice_k) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (kt * slice_k + kcol[i & 1] >= K) *(LDS_AS u32x4 *)(slot + (wave * NI + i) * 1024 + 16 * lane) = u32x4{};
   }
 };
 
@@ -293,10 +315,15 @@ struct MNLoader {
     }
   }
 
-  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int i) const {
-    const bool ok = kt * 64 + krow0 + RPI * i < K;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
-                                             ok ? off[i] : kOOB, (uint32_t)kt * slice_bytes, 0, 0);
+  // Instruction i of slice kt.  K rows are not checked: the rows of the
+  // ragged last slice at or past K lie past the end of the resource, so the
+  // range check returns zeros for them (the host keeps whole slices of rows
+  // inside 31-bit offsets, so no offset wraps).  A slice past the last one
+  // re-reads the last (its slot is never read).
+  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int nk, int i) const {
+    const int ks = kt < nk ? kt : (nk > 0 ? nk - 1 : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16, off[i],
+                                             (uint32_t)ks * slice_bytes, 0, 0);
   }
 };
 
@@ -359,7 +386,9 @@ struct Kernel {
   // fp6 (about 3% fewer cycles than three quarters and a half).
   static constexpr bool kFp46 = T::kDt == kFp4 || T::kFp6;
   static constexpr int kBarrierAt = T::kDt == kFp8 ? kMfma * 3 / 4 : kMfma / 2;
+  static constexpr int kFreeAt = kBarrierAt;
   static constexpr int kWindow = kFp46 ? kMfma * 3 / 4 : kMfma / 2;
+  static_assert(kFreeAt >= kNR && kFreeAt <= kBarrierAt, "slot-free barrier after this slice's reads");
   static_assert(kBarrierAt + kNR <= kMfma, "next-slice fragment reads must fit after the barrier");
   static_assert(kNR <= kBarrierAt, "this slice's second-substep reads come before the barrier");
   static_assert(kWindow <= kMfma && kWindow >= kLoads, "load window");
@@ -376,28 +405,30 @@ struct Kernel {
   // issued.  The workgroups of an XCD that share a panel split its lines
   // between them.  Measured: 7% fewer cycles for fp8; none for the 16-bit
   // kinds, which do not use it.
-  static constexpr int kLastLoad = kBarrierAt + (kLoads - 1) * kWindow / kLoads;
+  static constexpr int kLastLoad = kFreeAt + (kLoads - 1) * kWindow / kLoads;
   static constexpr bool kPfHead = kLastLoad >= kMfma;  // last load in the next slice's head
   static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
   // (Not for fp6: its three-slot ring already loads slice kt + 3 in slice kt.)
   static constexpr int kPfDist = T::kScaled && !T::kFp6 ? 3 : 0;
   static_assert(kPfDist == 0 || !kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
   static_assert(kPfDist == 0 || kPfHead || kPfAt < kMfma, "prefetch position");
+  static_assert(kPfDist == 0 || kFreeAt == kBarrierAt, "the prefetch placement assumes one barrier per slice");
 
-  // Loads of a slice issued in the tail of the slice kNS before it.
-  static constexpr int tail_loads() {
+  // Loads of a slice issued in the tail of the slice kNS before it, before
+  // MFMA `end` of that slice.
+  static constexpr int tail_loads(int end = kMfma) {
     int n = 0;
-    for (int i = 0; i < kLoads; ++i) n += kBarrierAt + i * kWindow / kLoads < kMfma;
+    for (int i = 0; i < kLoads; ++i) n += kFreeAt + i * kWindow / kLoads < end;
     return n;
   }
 
   // Which load (0 .. kLoads - 1) of slice kt + kNS (TAIL, positions >=
-  // kBarrierAt of slice kt) or of slice kt + kNS - 1 (positions <
-  // kBarrierAt of slice kt, the continuation of the window opened in slice
-  // kt - 1) goes out at MFMA Q; -1 for none.
+  // kFreeAt of slice kt) or of slice kt + kNS - 1 (positions < kFreeAt of
+  // slice kt, the continuation of the window opened in slice kt - 1) goes
+  // out at MFMA Q; -1 for none.
   static constexpr int load_at(int Q, bool tail) {
     for (int i = 0; i < kLoads; ++i) {
-      const int pos = kBarrierAt + i * kWindow / kLoads;
+      const int pos = kFreeAt + i * kWindow / kLoads;
       if (tail && pos == Q) return i;
       if (!tail && pos - kMfma == Q) return i;
     }
@@ -416,6 +447,7 @@ struct Kernel {
   int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
+  int zt;  // the ragged last slice (or the only, all-zero one when K = 0); -1 if none
   typename std::conditional<T::kFp6, DenseLoader<kLA>,
                             typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type>::type la;
   typename std::conditional<T::kFp6, DenseLoader<kLB>,
@@ -609,16 +641,36 @@ struct Kernel {
   template <int S>
   __device__ __forceinline__ void load_one(int kt, int i) {
     if (i < kLA) {
-      if constexpr (T::kAK)
+      if constexpr (T::kFp6)
         la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
+      else if constexpr (T::kDt == kFp8)
+        la.issue_masked(slots.a[S], wave, kt, a.K, kSliceK, i);
+      else if constexpr (T::kAK)
+        la.issue(slots.a[S], wave, kt, i);
       else
-        la.issue(slots.a[S], wave, kt, a.K, i);
+        la.issue(slots.a[S], wave, kt, nk, i);
     } else {
-      if constexpr (T::kBK)
+      if constexpr (T::kFp6)
         lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
+      else if constexpr (T::kDt == kFp8)
+        lb.issue_masked(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
+      else if constexpr (T::kBK)
+        lb.issue(slots.b[S], wave, kt, i - kLA);
       else
-        lb.issue(slots.b[S], wave, kt, a.K, i - kLA);
+        lb.issue(slots.b[S], wave, kt, nk, i - kLA);
     }
+  }
+
+  // Zero the chunks of the ragged last slice kt (in slot S) past column K,
+  // after this wave's loads of it have landed and before the barrier that
+  // lets the workgroup read it.  (K-major operands need nothing: their rows
+  // past K read as zeros.  MXFP8 and MXFP6 check columns in their loads.)
+  static constexpr bool kZeroTail = !T::kFp6 && T::kDt != kFp8 && (T::kAK || T::kBK);
+  template <int S>
+  __device__ __forceinline__ void zero_tail(int kt) {
+    if constexpr (T::kAK && !T::kFp6) la.zero_tail(slots.a[S], wave, lane, kt, a.K, kSliceK);
+    if constexpr (T::kBK && !T::kFp6) lb.zero_tail(slots.b[S], wave, lane, kt, a.K, kSliceK);
+    wait_vm_lgkm0<63>();
   }
 
   // One dword of each 128-byte line of slice kt of this workgroup's share of
@@ -729,12 +781,20 @@ struct Kernel {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
     constexpr int H = q % kHalves, I = q / kHalves / kNBm, J = q / kHalves % kNBm;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
+    if constexpr (kFreeAt < kBarrierAt && Q == kFreeAt) {
+      // Every wave's reads of this slot are done: its loads may start.
+      wait_vm_lgkm0<63>();
+      barrier();
+    }
     if constexpr (Q == kBarrierAt) {
       // The prefetch issued after the last needed load may be outstanding
       // (none precedes the first slice's barrier in the tail placement).
-      // The loads of slices kt + 2 .. kt + kNS - 1 may be outstanding too.
+      // The loads of slices kt + 2 .. kt + kNS - 1 may be outstanding too,
+      // and those of slice kt + kNS issued since kFreeAt (the newest).
       constexpr int kPfOut = kPfDist > 0 && (kPfHead || !FIRST) ? 1 : 0;
-      wait_vm_lgkm0<(kNS - 2) * kLoads + kPfOut>();
+      wait_vm_lgkm0<(kNS - 2) * kLoads + kPfOut + tail_loads(kBarrierAt)>();
+      if constexpr (kZeroTail)
+        if (kt + 1 == zt) zero_tail<(S + 1) % kNS>(kt + 1);
       barrier();
       // fp4: the scales of slice kt + 1 into the next set.  An odd slice
       // ends chunk (kt + 1) / 2: the next chunk moves up and the one after
@@ -799,6 +859,7 @@ struct Kernel {
     n0 = tn * TN;
     const int K = a.K;
     nk = a.ksteps;
+    zt = a.K % kSliceK != 0 || nk == 0 ? (nk > 0 ? nk - 1 : 0) : -1;
 
     if constexpr (T::kFp6)
       la.init(a.A + (size_t)m0 * a.lda, min(a.M - m0, TM), K, a.lda, wave, lane);
@@ -875,6 +936,8 @@ struct Kernel {
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) load_one<kNS - 1>(kNS - 1, i);
     wait_vm_lgkm0<(kNS - 2) * kLoads + kTailLoads>();
+    if constexpr (kZeroTail)
+      if (zt == 0) zero_tail<0>(0);
     if constexpr (T::kScaled) {
       if constexpr (T::kDt == kFp8)
         convert_scales(0);

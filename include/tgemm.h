@@ -84,7 +84,8 @@ TGEMM_API int gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
  * Each output is the fp32 sum over k of A[m][k] * B[k][n], rounded to
  * nearest-even fp16 (overflow gives +-inf).  K == 0 writes zeros.
  * Requirements: K % 8 == 0, N % 8 == 0, 16-byte aligned pointers,
- * 256 * K * 2 < 2^31 and K * N * 2 < 2^31.
+ * 256 * K * 2 < 2^31 and K' * N * 2 < 2^31, where K' is K rounded up to a
+ * multiple of 64 (B is read in whole slices of 64 rows).
  */
 TGEMM_API int gemm_f16_nn(int64_t M, int64_t N, int64_t K,
                 const void *A, const void *B, void *C, hipStream_t stream);
@@ -203,8 +204,8 @@ TGEMM_API int gemm_mxfp6_nt(int fmt, int64_t M, int64_t N, int64_t K,
  * stored row lengths and multiples of 8; the contiguous dimension of each
  * stored operand (K or M for A, N or K for B) and N multiples of 8; A, B
  * and C 16-byte aligned and C not overlapping A or B; a K-contiguous
- * operand's 256 rows and an M/N-contiguous operand as a whole below 2^31
- * bytes.
+ * operand's 256 rows, and an M/N-contiguous operand's K rows rounded up to
+ * a multiple of 64 (times its row stride), below 2^31 bytes.
  */
 TGEMM_API int gemm_bf16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
                         const void *A, int64_t lda, const void *B, int64_t ldb,
