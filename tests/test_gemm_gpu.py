@@ -246,8 +246,8 @@ def test_mxfp8_unaligned_scales_long_K(offset):
 
 
 def test_mxfp8_next_rows_scales_do_not_leak():
-    """K = 768: 6 slices of 128, run as 8 (the last two all zeros), whose
-    scale bytes would be the next row's.  Odd rows of A and B get 0xff
+    """K = 768: 6 slices of 128; a scale dword covers 4 slices, so the
+    second one's last two bytes would be the next row's.  Odd rows of A and B get 0xff
     scales (NaN in the e8m0 format); the products of even rows and even
     columns use none of them and must equal the oracle bit for bit."""
     M, N, K = 64, 64, 768
