@@ -140,6 +140,19 @@ def test_too_big():
     assert _bf16(1 << 31, 16, 16) == tg.ETOOBIG and "below 2^31" in tg.last_error()
 
 
+def test_k_major_operands_count_whole_slices_of_rows():
+    """A K-major operand is read in whole slices of 64 K rows (the rows past K
+    read as out of range), so K rounded up to 64, times the row stride, must
+    fit 31-bit offsets, not just the K rows themselves."""
+    far = 0x7F0000000000
+    K, N = 16328, 1 << 16
+    assert K * N * 2 < 2**31 - 1 < (K + 63) // 64 * 64 * N * 2
+    assert _f16(16, N, K, C=far) == tg.ETOOBIG and "B too large" in tg.last_error()
+    for fn in ("gemm_bf16", "gemm_f16"):
+        assert _g(1, 0, 16, 16, K, N, 16, 16, C=far, fn=fn) == tg.ETOOBIG and "A too large" in tg.last_error()
+        assert _g(0, 0, 16, N, K, K, N, N, C=far, fn=fn) == tg.ETOOBIG and "B too large" in tg.last_error()
+
+
 def test_error_message_resets_after_success():
     assert _bf16(-1, 1, 1) == tg.EINVAL and tg.last_error() != ""
     assert _bf16(0, 8, 8) == tg.OK and tg.last_error() == ""
