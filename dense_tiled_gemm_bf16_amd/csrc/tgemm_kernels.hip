@@ -483,7 +483,13 @@ struct Kernel {
   uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
   u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction
-  int sc_nxt[8], sc_cur[8];       // per block (4 x blocks, then 4 y blocks): bytes of 4 slices / groups
+  // Per block (4 x blocks, then 4 y blocks): fp8, the bytes of a group of 4
+  // slices, converted into sc_nxt and copied into sc_cur before the group's
+  // first slice.  fp4 and fp6 convert every slice's scales straight into
+  // the set its MFMAs read (fp4: set kt % 2, fp6: set kt % 3, the slot), so
+  // no copy is needed at the start of a slice.
+  int sc_nxt[8], sc_cur[8];
+  int sc_set[3][8];
   Acc acc[kNBn][kNBm];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
@@ -647,7 +653,7 @@ struct Kernel {
     if (i < kLA) {
       if constexpr (T::kFp6)
         la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
-      else if constexpr (T::kDt == kFp8 && !T::kWholeK)
+      else if constexpr (T::kScaled && !T::kWholeK)
         la.issue_masked(slots.a[S], wave, kt, a.K, kSliceK, i);
       else if constexpr (T::kAK)
         la.issue(slots.a[S], wave, kt, i);
@@ -656,7 +662,7 @@ struct Kernel {
     } else {
       if constexpr (T::kFp6)
         lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
-      else if constexpr (T::kDt == kFp8 && !T::kWholeK)
+      else if constexpr (T::kScaled && !T::kWholeK)
         lb.issue_masked(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
       else if constexpr (T::kBK)
         lb.issue(slots.b[S], wave, kt, i - kLA);
@@ -669,7 +675,7 @@ struct Kernel {
   // after this wave's loads of it have landed and before the barrier that
   // lets the workgroup read it.  (K-major operands need nothing: their rows
   // past K read as zeros.  MXFP8 and MXFP6 check columns in their loads.)
-  static constexpr bool kZeroTail = !T::kFp6 && T::kDt != kFp8 && (T::kAK || T::kBK);
+  static constexpr bool kZeroTail = !T::kScaled && (T::kAK || T::kBK);
   template <int S>
   __device__ __forceinline__ void zero_tail(int kt) {
     if constexpr (T::kAK && !T::kFp6) la.zero_tail(slots.a[S], wave, lane, kt, a.K, kSliceK);
@@ -703,15 +709,22 @@ struct Kernel {
   }
 
   // fp4: slice t's 8 scale bytes per row, from chunk t / 2 (ODD: t odd, its
-  // second half, plus the next chunk's first dword), into sc_nxt.
-  template <bool ODD>
+  // second half, plus the next chunk's first dword), into sc_set[DST].  The
+  // two chunk buffers take turns: buffer CUR (0: sc_ck, 1: sc_ckn) holds
+  // chunk t / 2 and the other one the chunk after it.  Once an odd slice has
+  // been converted, chunk t / 2 is done with and chunk t / 2 + 2 is loaded
+  // into its buffer, so no register is ever copied to another: a copy at the
+  // loop's back edge waited for that load (18% of the cycles).
+  template <bool ODD, int CUR, int DST>
   __device__ __forceinline__ void convert_scales4(int t) {
     const uint32_t keep0 = keep_mask(a.kb - 8 * t), keep1 = keep_mask(a.kb - 8 * t - 4);
+    u32x4(&cur)[4] = CUR == 0 ? sc_ck : sc_ckn;
+    u32x4(&nxt)[4] = CUR == 0 ? sc_ckn : sc_ck;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w0 = ODD ? sc_ck[j][2] : sc_ck[j][0];
-      const uint32_t w1 = ODD ? sc_ck[j][3] : sc_ck[j][1];
-      const uint32_t w2 = ODD ? sc_ckn[j][0] : sc_ck[j][2];
+      const uint32_t w0 = ODD ? cur[j][2] : cur[j][0];
+      const uint32_t w1 = ODD ? cur[j][3] : cur[j][1];
+      const uint32_t w2 = ODD ? nxt[j][0] : cur[j][2];
       const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sc_sh[j]) & keep0;
       const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sc_sh[j]) & keep1;
       const uint32_t lo = __builtin_amdgcn_perm(d1, d0, 0x05040100u);  // groups 0, 1, 4, 5
@@ -719,9 +732,10 @@ struct Kernel {
       // Block 2 j: lo of rows 0-31 in lanes 0-31, hi of the same rows in
       // lanes 32-63; block 2 j + 1 likewise for rows 32-63.
       const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
-      sc_nxt[2 * j] = (int)sw[0];
-      sc_nxt[2 * j + 1] = (int)sw[1];
+      sc_set[DST][2 * j] = (int)sw[0];
+      sc_set[DST][2 * j + 1] = (int)sw[1];
     }
+    if constexpr (ODD) load_chunks(cur, t / 2 + 2);
   }
 
   // fp8: group g, shifted out of the window's first two dwords and
@@ -753,6 +767,7 @@ struct Kernel {
   // w uses group 2 s + w, so lanes 0-31 take groups 0, 2 and lanes 32-63
   // groups 1, 3, in byte s.  After a chunk's last slice the next chunk
   // moves up and the one after it is loaded (three slices ahead of use).
+  // Into sc_set[POS], the set slice t (in slot POS) reads.
   template <int POS>
   __device__ __forceinline__ void convert_scales6(int t) {
     const uint32_t keep = keep_mask(a.kb - 4 * t);
@@ -762,8 +777,8 @@ struct Kernel {
       const uint32_t lo = __builtin_amdgcn_perm(0u, d, 0x0c0c0200u);  // groups 0, 2
       const uint32_t hi = __builtin_amdgcn_perm(0u, d, 0x0c0c0301u);  // groups 1, 3
       const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
-      sc_nxt[2 * j] = (int)sw[0];
-      sc_nxt[2 * j + 1] = (int)sw[1];
+      sc_set[POS][2 * j] = (int)sw[0];
+      sc_set[POS][2 * j + 1] = (int)sw[1];
     }
     if constexpr (POS == 2) {
 #pragma unroll
@@ -800,19 +815,13 @@ struct Kernel {
       if constexpr (kZeroTail)
         if (kt + 1 == zt) zero_tail<(S + 1) % kNS>(kt + 1);
       barrier();
-      // fp4: the scales of slice kt + 1 into the next set.  An odd slice
-      // ends chunk (kt + 1) / 2: the next chunk moves up and the one after
-      // it is loaded (waited for by the next barrier, used after the one
-      // after).
+      // fp4: the scales of slice kt + 1 into the next set, from the chunk
+      // buffer that holds them (JB = kt % 4: slices 4 i + 2 and 4 i + 3 read
+      // sc_ck, 4 i + 4 and 4 i + 5 sc_ckn).  An odd slice ends its chunk,
+      // whose buffer then takes the chunk after the next (waited for by the
+      // next barrier, used after the one after).
       if constexpr (T::kFp6) convert_scales6<(S + 1) % 3>(kt + 1);
-      if constexpr (T::kDt == kFp4) {
-        convert_scales4<(JB & 1) == 0>(kt + 1);
-        if constexpr ((JB & 1) == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sc_ck[j] = sc_ckn[j];
-          load_chunks(sc_ckn, (kt >> 1) + 2);
-        }
-      }
+      if constexpr (T::kDt == kFp4) convert_scales4<(JB & 1) == 0, JB == 1 || JB == 2 ? 0 : 1, (JB + 1) & 1>(kt + 1);
     }
     if constexpr (Q < kNR) read_one<S, Q>(f1, 1);
     if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNR) read_one<(S + 1) % kNS, Q - kBarrierAt>(f0, 0);
@@ -821,10 +830,10 @@ struct Kernel {
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
     const Frags &f = SUB == 0 ? f0 : f1;
     if constexpr (T::kDt == kFp4)
-      acc[I][J] = mma<FIRST && SUB == 0 && H == 0, 2 * SUB + H, H>(f.x[I], f.y[J], acc[I][J], sc_cur[I],
-                                                                   sc_cur[4 + J]);
+      acc[I][J] = mma<FIRST && SUB == 0 && H == 0, 2 * SUB + H, H>(f.x[I], f.y[J], acc[I][J], sc_set[JB & 1][I],
+                                                                   sc_set[JB & 1][4 + J]);
     else if constexpr (T::kFp6)
-      acc[I][J] = mma<FIRST && SUB == 0, SUB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
+      acc[I][J] = mma<FIRST && SUB == 0, SUB>(f.x[I], f.y[J], acc[I][J], sc_set[S][I], sc_set[S][4 + J]);
     else if constexpr (T::kScaled)
       acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
@@ -838,11 +847,11 @@ struct Kernel {
   }
 
   // One K slice kt from slot S (its substep-0 fragments already in f0); JB
-  // = kt % 4 for the block-scaled kind.
+  // = kt % 4 for the block-scaled kinds (fp6: the slot).
   template <int S, int JB, bool FIRST = false>
   __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
     if constexpr (T::kDt == kFp8 && JB == 3) convert_scales((kt + 1) >> 2);
-    if constexpr ((T::kDt == kFp8 && JB == 0 && !FIRST) || ((T::kDt == kFp4 || T::kFp6) && !FIRST)) {
+    if constexpr (T::kDt == kFp8 && JB == 0 && !FIRST) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
     }
@@ -931,6 +940,9 @@ struct Kernel {
     if constexpr (T::kFp6) {
       load_bytes16(sc_ck, 0);
       load_bytes16(sc_ckn, 12);
+    } else if constexpr (T::kDt == kFp4) {
+      load_chunks(sc_ckn, 0);
+      load_chunks(sc_ck, 1);
     } else if constexpr (T::kScaled) {
       load_chunks(sc_ck, 0);
       load_chunks(sc_ckn, 1);
@@ -942,25 +954,24 @@ struct Kernel {
     wait_vm_lgkm0<(kNS - 2) * kLoads + kTailLoads>();
     if constexpr (kZeroTail)
       if (zt == 0) zero_tail<0>(0);
-    if constexpr (T::kScaled) {
-      if constexpr (T::kDt == kFp8)
-        convert_scales(0);
-      else if constexpr (T::kFp6)
-        convert_scales6<0>(0);
-      else
-        convert_scales4<false>(0);
+    if constexpr (T::kDt == kFp8) {
+      convert_scales(0);
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
+    } else if constexpr (T::kFp6) {
+      convert_scales6<0>(0);
+    } else if constexpr (T::kDt == kFp4) {
+      convert_scales4<false, 1, 0>(0);
     }
     barrier();
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
     // Slice 0 starts the accumulators; then the slices go round the ring a
-    // whole number of slots at a time (fp8: four, for its scale groups),
+    // whole number of slots at a time (fp8 and fp4: four, for their scale chunks),
     // and the one to three left after the last round run on their own, so
     // no slice past nk is computed.
     step<0, 0, true>(0, f0, f1);
-    if constexpr (T::kDt == kFp8) {
+    if constexpr (T::kDt == kFp8 || T::kDt == kFp4) {
       int kt = 1;
       for (; kt + 3 < nk; kt += 4) {
         step<1, 1>(kt, f0, f1);
@@ -1263,7 +1274,8 @@ hipError_t launch(const Problem &p) {
       break;
     case Dt::kMxfp4:
       if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
-        return launch_shape<Traits<kFp4, true, true>, 256, 256>(p, a);
+        return p.K > 0 && p.K % 256 == 0 ? launch_shape<Traits<kFp4, true, true, true>, 256, 256>(p, a)
+                                         : launch_shape<Traits<kFp4, true, true>, 256, 256>(p, a);
       break;
     case Dt::kMxfp6E2M3:
       if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
