@@ -1,11 +1,12 @@
 // Tiled dense GEMM kernels for gfx950 (MI355X, CDNA4).
 //
 // One workgroup of 256 threads (4 wave64s in a 2 x 2 grid) computes a
-// TM x TN tile of C -- 256 x 256, or 256 x 192 and 128 x 128 where that
-// fills the chip better -- and each wave a TM/2 x TN/2 sub-tile of fp32
+// TM x TN tile of C -- 256 x 256, or 256 x 192, 128 x 128 and 64 x 64 where
+// that fills the chip better -- and each wave a TM/2 x TN/2 sub-tile of fp32
 // accumulators (in AGPRs; 256 per lane for 256 x 256).  The K loop walks
-// 128-byte slices of the A and B panels (64 bf16/fp16 or 128 fp8 elements
-// per row) through two LDS slots per operand.
+// slices of the A and B panels (128 bytes of a row: 64 bf16/fp16, 128 fp8
+// or 256 fp4 elements; 96 bytes, 128 elements, for fp6) through a ring of
+// LDS slots per operand.
 //
 // Where this follows the pages and where it departs:
 //  * tile grid: ceil-div over N and M as in the TileLang SM100 README
@@ -20,22 +21,25 @@
 //    16 bytes with a buffer load that writes LDS directly, a whole 128-byte
 //    line per row and slice; the 16-byte chunks of each row are
 //    XOR-permuted so the MFMA operand reads hit distinct LDS banks.
-//    Out-of-range rows and the ragged K tail take an out-of-range buffer
-//    offset and arrive as zeros (the pages' TMA zero OOB fill).
+//    Out-of-range rows take an out-of-range buffer offset and arrive as
+//    zeros (the pages' TMA zero OOB fill).  The ragged last K slice of a
+//    K-contiguous operand is zeroed in LDS past column K once it has landed
+//    (MXFP8 with a ragged K, MXFP4 with a ragged K and MXFP6 check columns
+//    in their loads instead); a K-major operand's rows past K read as zeros.
 //  * pipelined K loop: the pages use a 3-slot ring with producer and
 //    consumer warpgroups and mbarrier parity waits (velog "tilelang",
 //    Device IRModule).  Here every wave both loads and computes, with a
-//    ring of NS slots (two for 256-row tiles, four for 128 x 128):
-//    partway through slice kt's MFMAs (halfway for 16-bit inputs, three
-//    quarters for fp8) a wait and a barrier free slot kt % NS; the loads of
-//    slice kt + NS into it then go out spread over the next half slice of
-//    MFMAs and have at least NS - 1.5 slices to land before they are
-//    needed.  The next slice's first operand reads follow the barrier,
-//    overlapping the current slice's remaining MFMAs.
+//    ring of NS slots (two for 256-row tiles, three for fp6, four for
+//    128 x 128 and 64 x 64): partway through slice kt's MFMAs (halfway, or
+//    three quarters for fp8) a wait and a barrier free slot kt % NS; the
+//    loads of slice kt + NS into it then go out spread over the next half
+//    slice of MFMAs (three quarters for fp4 and fp6).  The next slice's
+//    first operand reads follow the barrier, overlapping the current
+//    slice's remaining MFMAs.
 //  * wave-tile MMA: v_mfma_f32_16x16x32_{bf16,f16} (8 x 8 blocks per wave)
-//    and, for the block-scaled path, v_mfma_scale_f32_32x32x64_f8f6f4
+//    and, for the block-scaled kinds, v_mfma_scale_f32_32x32x64_f8f6f4
 //    (4 x 4 blocks) with the e8m0 block scales as operands (TCGEN05
-//    tutorial, "进阶" (Advanced)).
+//    tutorial, "进阶" (Advanced)), on fp8, fp6 or fp4 elements.
 //  * operand layouts (trans_A / trans_B of the SM100 README's T.gemm): an
 //    operand stored K-contiguous (A as M x K, B as N x K) is staged row by
 //    row as above; one stored M- or N-contiguous (A as K x M, B as K x N)
@@ -44,8 +48,8 @@
 //    column.  Rows of every operand and of C are ld elements apart.
 //  * epilogue: fp32 -> bf16/fp16 with round-to-nearest-even, masked stores.
 //    The MFMA is fed B rows as its first operand and A rows as its second,
-//    so each lane's accumulators hold 4 consecutive columns of one row of C
-//    and leave as one 8-byte store.
+//    so each lane's accumulators hold consecutive columns of one row of C;
+//    lane swaps regroup them so each lane leaves 16 bytes per store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -199,8 +203,7 @@ struct PanelLoader {
   int kcol[2];       // element column of this lane's chunk inside a slice (even / odd i)
   uint32_t slice_bytes;
 
-  // slice_k: elements of a row per slice (fp6: 96 bytes, so the slot
-  // rows' last two chunks stay unloaded).
+  // slice_k: elements of a row per slice (the 128 bytes of a slot row).
   __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int ld, int elem, int slice_k,
                                        int wave, int lane) {
     slice_bytes = (uint32_t)(slice_k * elem);
@@ -210,9 +213,7 @@ struct PanelLoader {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = wave * 8 * NI + i * 8 + (lane >> 3);
-      off[i] = r < rows_valid && kcol[i & 1] < slice_k
-                   ? (uint32_t)r * (uint32_t)ld * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem
-                   : kOOB;
+      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)ld * (uint32_t)elem + (uint32_t)kcol[i & 1] * elem : kOOB;
     }
   }
 
