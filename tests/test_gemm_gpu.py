@@ -368,3 +368,50 @@ def test_misaligned_device_pointer_is_rejected():
     c = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
     rc = tg.lib().gemm_bf16_nt(64, 64, 64, a.data_ptr() + 2, b.data_ptr(), c.data_ptr(), None)
     assert rc == tg.EALIGN and "A is not 16-byte aligned" in tg.last_error()
+
+
+def _classes(v):
+    """Per output: 0 finite, 1 +inf, 2 -inf, 3 NaN."""
+    return np.where(np.isnan(v), 3, np.where(v == np.inf, 1, np.where(v == -np.inf, 2, 0)))
+
+
+@pytest.mark.parametrize("tile", [(0, 0), (256, 256), (128, 128), (64, 64)])
+def test_special_values_match_the_oracle(tile, forced_tile):
+    """Infinities and NaN planted in A and B (bf16 NT, ragged sizes): every
+    output that the oracle makes +inf, -inf or NaN is the same on the GPU,
+    and the rest agree within the tolerance.  (IEEE semantics do not depend
+    on the summation order: inf + finite = inf, inf - inf = NaN, NaN stays.)"""
+    forced_tile(*tile)
+    M, N, K = 300, 264, 200
+    x = workloads.make_random("bf16_nt", M, N, K, seed=21)
+    A, B = x["A"].copy(), x["B"].copy()
+    PINF, NINF, NAN = 0x7F80, 0xFF80, 0x7FC0
+    A[5, 17] = PINF                 # row 5: +-inf by the sign of B[n, 17]
+    A[40, 3], A[40, 150] = PINF, NINF   # row 40: NaN unless B cancels one term
+    A[299, 199] = NAN               # the last row, the last (ragged) K column
+    B[7, 60] = NINF                 # column 7
+    B[263, 0] = NAN                 # the last column
+    x["A"], x["B"] = A, B
+    got = values("bf16_nt", to_bits(run("bf16_nt", x, M, N, K)))
+    ref = values("bf16_nt", oracle_full("bf16_nt", x))
+    gc, rc = _classes(got), _classes(ref)
+    assert (rc != 0).sum() > M + N, "the planted values should reach whole rows and columns"
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{len(bad)} outputs differ in class, first {bad[0]}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
+    fin = rc == 0
+    ok = np.abs(got[fin] - ref[fin]) <= ATOL + RTOL * np.abs(ref[fin])
+    assert ok.all(), f"{int((~ok).sum())} finite outputs outside tolerance"
+
+
+def test_fp16_overflow_gives_infinity():
+    """fp16 NN: sums past 65504 round to +-inf, as the oracle's one rounding does."""
+    M, N, K = 64, 72, 136
+    A = np.full((M, K), 0x5000, np.uint16)      # 32.0
+    A[1::2] = 0xD000                            # -32.0 on odd rows
+    B = np.full((K, N), 0x5000, np.uint16)
+    B[:, 5] = 0x2C00                            # 0.0625: column 5 stays finite (272)
+    x = {"A": A, "B": B}
+    got = to_bits(run("f16_nn", x, M, N, K))
+    ref = oracle_full("f16_nn", x)
+    assert np.array_equal(got, ref)
+    assert np.all(got[0::2, 0] == 0x7C00) and np.all(got[1::2, 0] == 0xFC00) and np.all(np.abs(f16_values(got[:, 5])) == 272)

@@ -9,7 +9,9 @@
   at the workloads' shapes;
 * the sampled (one output at a time) entry points equal the full ones;
 * block-scaled FP8: exact rational sums, the scale index k/128 per row,
-  the e8m0 bias, and scale factoring (one more exponent doubles C exactly).
+  the e8m0 bias, and scale factoring (one more exponent doubles C exactly);
+* IEEE special values: infinities and NaN in the inputs, and a finite sum
+  past the output format's largest value.
 """
 from fractions import Fraction
 
@@ -288,3 +290,33 @@ def test_mxfp8_4096_sampled_exact():
                     Fraction(0))
         assert Fraction(out64[p]) == exact
         assert Fraction(float(bf16_values(out[p:p + 1])[0])) == rne(exact, **BF16)
+
+
+# --- IEEE special values -------------------------------------------------------
+
+def test_special_values_follow_ieee():
+    """An infinite element makes its outputs infinite with the sign of the
+    product (NaN where the other factor is 0); +inf and -inf terms give NaN;
+    a NaN element gives NaN; a finite sum past the output format's largest
+    value rounds to infinity (fp16: 128 products of 32 * 32 = 131072 >
+    65504)."""
+    M, N, K = 4, 3, 8
+    A = np.ones((M, K), np.float32)
+    B = np.ones((N, K), np.float32)
+    B[1, 2], B[2, 2] = -1.0, 0.0
+    A[0, 2] = np.inf                          # row 0: +inf, -inf, inf * 0 = NaN
+    A[1, 4], A[1, 5] = np.inf, -np.inf        # row 1: inf - inf = NaN
+    A[2, 6] = np.nan                          # row 2: NaN
+    C = bf16_values(oracle.gemm_bf16_nt(_bf16(A), _bf16(B)))
+    assert C[0, 0] == np.inf and C[0, 1] == -np.inf and np.isnan(C[0, 2])
+    assert np.isnan(C[1]).all() and np.isnan(C[2]).all()
+    assert list(C[3]) == [8.0, 6.0, 7.0]      # row 3: finite, B's -1 and 0 at k = 2
+    Ah = np.full((2, 128), 32.0, np.float32)
+    Ah[1] = -32.0
+    Bh = np.full((128, 2), 32.0, np.float32)
+    Ch = f16_values(oracle.gemm_f16_nn(_f16(Ah), _f16(Bh)))
+    assert (Ch[0] == np.inf).all() and (Ch[1] == -np.inf).all()
+    Ch = f16_values(oracle.gemm_f16_nn(_f16(Ah[:, :127]), _f16(Bh[:127])))
+    assert (Ch[0] == np.inf).all()            # 130048: still past 65504
+    Ch = f16_values(oracle.gemm_f16_nn(_f16(Ah[:, :63]), _f16(Bh[:63])))
+    assert (Ch[0] == 64512.0).all()           # 64512 is an fp16 value: no overflow
