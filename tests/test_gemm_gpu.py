@@ -415,3 +415,20 @@ def test_fp16_overflow_gives_infinity():
     ref = oracle_full("f16_nn", x)
     assert np.array_equal(got, ref)
     assert np.all(got[0::2, 0] == 0x7C00) and np.all(got[1::2, 0] == 0xFC00) and np.all(np.abs(f16_values(got[:, 5])) == 272)
+
+
+def test_mxfp8_nan_element_and_nan_scale_propagate():
+    """A NaN e4m3fn element (0x7F) and a NaN e8m0 scale (0xFF) make their
+    rows' and columns' outputs NaN on the GPU exactly where the oracle's do;
+    the rest match bit for bit (integer elements, unit scales)."""
+    M, N, K = 264, 136, 384
+    x = workloads.make_integer("mxfp8_nt", M, N, K, seed=23)
+    x["qA"][3, 200] = 0x7F              # row 3
+    x["sB"][70, 2] = 0xFF               # column 70 (its third 128-K block)
+    got = to_bits(run("mxfp8_nt", x, M, N, K))
+    ref = oracle_full("mxfp8_nt", x)
+    g, r = bf16_values(got), bf16_values(ref)
+    assert np.isnan(r[3]).all() and np.isnan(r[:, 70]).all()
+    assert np.array_equal(np.isnan(g), np.isnan(r))
+    fin = ~np.isnan(r)
+    assert np.array_equal(got[fin], ref[fin])
