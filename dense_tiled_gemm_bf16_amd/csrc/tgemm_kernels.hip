@@ -1045,25 +1045,41 @@ struct Kernel {
       // 32 x 32 blocks: lanes l and l + 32 hold the same row, columns
       // 8 g .. 8 g + 3 and 8 g + 4 .. 8 g + 7 of group g.  One swap of the
       // wave halves per pair of groups (2 p, 2 p + 1) gives lane l columns
-      // 16 p .. 16 p + 7 and lane l + 32 columns 16 p + 8 .. 16 p + 15, so
-      // each lane leaves 16 bytes per store and a store instruction writes
-      // 32 contiguous bytes of each of 32 rows.  (Every lane swaps; only the
+      // 16 p .. 16 p + 7 and lane l + 32 columns 16 p + 8 .. 16 p + 15 (X
+      // for p = 0, Y for p = 1).  A swap of odd and even 16-lane rows of X
+      // and Y then leaves the 16-lane rows of the wave with (X_0 Y_0 X_2 Y_2)
+      // -- the 32 columns of block rows 0-15 -- and (X_1 Y_1 X_3 Y_3), those
+      // of rows 16-31: each store instruction writes 64 contiguous bytes of
+      // each of 16 rows, four lanes per row.  (Every lane swaps; only the
       // stores are masked.)
-      const int half = lane >> 5;
+      const int r16 = lane & 15;
+      const int col = 16 * ((lane >> 4) & 1) + 8 * (lane >> 5);
 #pragma unroll
       for (int j = 0; j < kNBm; ++j) {
-        const int m = m0 + wave_m * kWM + j * kBlk + row_l;
-        uint8_t *crow = a.C + (size_t)m * a.ldc * 2;
+        const int m = m0 + wave_m * kWM + j * kBlk + r16;
+        uint8_t *crow0 = a.C + (size_t)m * a.ldc * 2;
+        uint8_t *crow1 = a.C + (size_t)(m + 16) * a.ldc * 2;
 #pragma unroll
         for (int i = 0; i < kNBn; ++i) {
+          u32x4 xy[2];
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
             const u32x2 p0 = pack4(acc[i][j], 8 * pr), p1 = pack4(acc[i][j], 8 * pr + 4);
             const auto s0 = __builtin_amdgcn_permlane32_swap(p0[0], p1[0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(p0[1], p1[1], false, false);
-            const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
-            const int n = n0 + wave_n * kWN + i * kBlk + 16 * pr + 8 * half;
-            if (m < a.M && n < a.N) *(u32x4 *)(crow + (size_t)n * 2) = out;
+            xy[pr] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+          }
+          u32x4 lo, hi;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const auto r = __builtin_amdgcn_permlane16_swap(xy[0][d], xy[1][d], false, false);
+            lo[d] = r[0];
+            hi[d] = r[1];
+          }
+          const int n = n0 + wave_n * kWN + i * kBlk + col;
+          if (n < a.N) {
+            if (m < a.M) *(u32x4 *)(crow0 + (size_t)n * 2) = lo;
+            if (m + 16 < a.M) *(u32x4 *)(crow1 + (size_t)n * 2) = hi;
           }
         }
       }
