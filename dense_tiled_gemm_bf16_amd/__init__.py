@@ -3,7 +3,8 @@
 Argument marshalling only: every step of the GEMM runs in the library's
 gfx950 kernels.  The functions here check tensor dtypes, shapes and
 contiguity, allocate the output when none is given, and call the C entry
-point of the same name on the current HIP stream.  There is no fallback:
+point of the same name on the device the tensors live on, on that device's
+current HIP stream unless a stream is given.  There is no fallback:
 if libtgemm.so is missing the import of the library fails loudly.
 
 The C ABI itself is declared in include/tgemm.h; ``lib()`` returns the
@@ -87,11 +88,31 @@ def _torch():
     return torch
 
 
-def _stream_ptr(stream):
+def _stream_ptr(stream, device):
     torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _same_device(**named):
+    """The one device all the named tensors live on (raises otherwise)."""
+    devs = {n: t.device for n, t in named.items()}
+    first = next(iter(devs.values()))
+    for n, d in devs.items():
+        if d != first:
+            raise ValueError(f"{n} is on {d}, not on {first} with the other operands")
+    return first
+
+
+def _call(fn, device, stream, *args):
+    """Call a C entry point with the tensors' device current (the library
+    sets up and launches on the current device) and check its status."""
+    torch = _torch()
+    with torch.cuda.device(device):
+        check(fn(*args, _stream_ptr(stream, device)))
 
 
 def _want(t, name, dtype, shape):
@@ -124,7 +145,8 @@ def gemm_bf16_nt(a, b, out=None, stream=None):
     _want(a, "a", torch.bfloat16, (M, K))
     _want(b, "b", torch.bfloat16, (N, K))
     c = _out(out, (M, N), torch.bfloat16, a)
-    check(lib().gemm_bf16_nt(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    dev = _same_device(a=a, b=b, out=c)
+    _call(lib().gemm_bf16_nt, dev, stream, M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr())
     return c
 
 
@@ -136,7 +158,8 @@ def gemm_f16_nn(a, b, out=None, stream=None):
     _want(a, "a", torch.float16, (M, K))
     _want(b, "b", torch.float16, (K, N))
     c = _out(out, (M, N), torch.float16, a)
-    check(lib().gemm_f16_nn(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    dev = _same_device(a=a, b=b, out=c)
+    _call(lib().gemm_f16_nn, dev, stream, M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr())
     return c
 
 
@@ -159,8 +182,9 @@ def gemm_mxfp8_nt(a, b, scale_a, scale_b, out=None, stream=None):
     _want(scale_a, "scale_a", torch.uint8, (M, KB))
     _want(scale_b, "scale_b", torch.uint8, (N, KB))
     c = _out(out, (M, N), torch.bfloat16, a)
-    check(lib().gemm_mxfp8_nt(M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
-                              scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    dev = _same_device(a=a, b=b, scale_a=scale_a, scale_b=scale_b, out=c)
+    _call(lib().gemm_mxfp8_nt, dev, stream, M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
+          scale_b.data_ptr(), c.data_ptr())
     return c
 
 
@@ -173,7 +197,8 @@ def quantize_mxfp8(x, q=None, scales=None, stream=None):
     _want(x, "x", torch.float32, (M, K))
     q = _out(q, (M, K), torch.uint8, x)
     scales = _out(scales, (M, KB), torch.uint8, x)
-    check(lib().quantize_mxfp8(M, K, x.data_ptr(), q.data_ptr(), scales.data_ptr(), _stream_ptr(stream)))
+    dev = _same_device(x=x, q=q, scales=scales)
+    _call(lib().quantize_mxfp8, dev, stream, M, K, x.data_ptr(), q.data_ptr(), scales.data_ptr())
     return q, scales
 
 
@@ -214,8 +239,9 @@ def gemm(a, b, out=None, stream=None):
     if out.dtype != a.dtype or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1):
         raise ValueError("out must be a row-major (M, N) tensor of the input dtype")
     ldc = max(out.stride(0), N)
+    dev = _same_device(a=a, b=b, out=out)
     fn = lib().gemm_bf16 if a.dtype == torch.bfloat16 else lib().gemm_f16
-    check(fn(ta, tb, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, _stream_ptr(stream)))
+    _call(fn, dev, stream, ta, tb, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc)
     return out
 
 
@@ -234,8 +260,9 @@ def gemm_mxfp4_nt(a, b, scale_a, scale_b, out=None, stream=None):
     _want(scale_a, "scale_a", torch.uint8, (M, K // 32))
     _want(scale_b, "scale_b", torch.uint8, (N, K // 32))
     c = _out(out, (M, N), torch.bfloat16, a)
-    check(lib().gemm_mxfp4_nt(M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
-                              scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    dev = _same_device(a=a, b=b, scale_a=scale_a, scale_b=scale_b, out=c)
+    _call(lib().gemm_mxfp4_nt, dev, stream, M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
+          scale_b.data_ptr(), c.data_ptr())
     return c
 
 
@@ -252,6 +279,8 @@ def gemm_mxfp6_nt(a, b, scale_a, scale_b, fmt="e2m3", out=None, stream=None):
     torch = _torch()
     M, RB = a.shape
     N = b.shape[0]
+    if RB % 3 != 0:
+        raise ValueError(f"a has {RB} bytes per row; packed FP6 rows hold 3 bytes per 4 elements")
     K = RB // 3 * 4
     if fmt not in FP6_FORMATS:
         raise ValueError(f"fmt must be one of {sorted(FP6_FORMATS)}")
@@ -260,6 +289,7 @@ def gemm_mxfp6_nt(a, b, scale_a, scale_b, fmt="e2m3", out=None, stream=None):
     _want(scale_a, "scale_a", torch.uint8, (M, K // 32))
     _want(scale_b, "scale_b", torch.uint8, (N, K // 32))
     c = _out(out, (M, N), torch.bfloat16, a)
-    check(lib().gemm_mxfp6_nt(FP6_FORMATS[fmt], M, N, K, a.data_ptr(), b.data_ptr(), scale_a.data_ptr(),
-                              scale_b.data_ptr(), c.data_ptr(), _stream_ptr(stream)))
+    dev = _same_device(a=a, b=b, scale_a=scale_a, scale_b=scale_b, out=c)
+    _call(lib().gemm_mxfp6_nt, dev, stream, FP6_FORMATS[fmt], M, N, K, a.data_ptr(), b.data_ptr(),
+          scale_a.data_ptr(), scale_b.data_ptr(), c.data_ptr())
     return c

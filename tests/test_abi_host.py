@@ -230,3 +230,21 @@ def test_general_entry_validation(fn):
     # 31-bit offsets: an M-contiguous A addressed as a whole.
     far = 0x7F0000000000
     assert _g(1, 0, 1 << 16, 16, 1 << 15, 1 << 16, 16, 16, C=far, fn=fn) == tg.ETOOBIG
+
+
+def test_wrapper_rejects_fp6_rows_that_are_not_whole_groups():
+    # 49 bytes per row is no whole number of 3-byte groups of four elements;
+    # the wrapper must refuse it before any pitch is derived from it.
+    import torch
+    a = torch.zeros((4, 49), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="3 bytes per 4 elements"):
+        tg.gemm_mxfp6_nt(a, a, a, a)
+
+
+def test_wrapper_requires_one_device():
+    import torch
+    a = torch.zeros(2, device="cpu")
+    b = torch.zeros(2, device="meta")
+    assert tg._same_device(a=a, x=a) == torch.device("cpu")
+    with pytest.raises(ValueError, match="b is on meta"):
+        tg._same_device(a=a, b=b)
