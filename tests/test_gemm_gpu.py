@@ -432,3 +432,57 @@ def test_mxfp8_nan_element_and_nan_scale_propagate():
     assert np.array_equal(np.isnan(g), np.isnan(r))
     fin = ~np.isnan(r)
     assert np.array_equal(got[fin], ref[fin])
+
+
+def test_graph_replays_match_eager():
+    # The entry points record only kernel launches (no memset, no
+    # allocation), so a caller may capture them into a HIP graph.  Each
+    # replay, with eager work and synchronisations between replays, must
+    # reproduce the eager outputs bit for bit, and must read the inputs as
+    # they are at replay time (the second pass doubles them: scaling by 2 is
+    # exact, so every output doubles exactly).
+    M, N, K = 520, 264, 1008                   # K ragged against the 64- and 128-element slices
+    xb = workloads.make_random("bf16_nt", M, N, K, seed=11)
+    a, b = to_dev(xb["A"], "bf16"), to_dev(xb["B"], "bf16")
+    g = torch.Generator().manual_seed(12)
+    xa32 = torch.randn(M, K, generator=g).cuda()
+    xb32 = torch.randn(N, K, generator=g).cuda()
+    KB = (K + 127) // 128
+    c16 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    c8 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    qa = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    qb = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M, KB, dtype=torch.uint8, device="cuda")
+    sb = torch.empty(N, KB, dtype=torch.uint8, device="cuda")
+
+    def work():
+        tg.gemm_bf16_nt(a, b, out=c16)
+        tg.quantize_mxfp8(xa32, q=qa, scales=sa)
+        tg.quantize_mxfp8(xb32, q=qb, scales=sb)
+        tg.gemm_mxfp8_nt(qa, qb, sa, sb, out=c8)
+
+    print(f"[gpu] graph capture bf16 NT + quantise + MXFP8 NT M={M} N={N} K={K}", flush=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref16, ref8 = c16.clone(), c8.clone()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        if rep == 2:
+            a.mul_(2)
+            xa32.mul_(2)
+            ref16, ref8 = ref16 * 2, ref8 * 2
+        for t in (c16, c8, qa, qb, sa, sb):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c16.view(torch.int16), ref16.view(torch.int16)), f"bf16 replay {rep}"
+        assert torch.equal(c8.view(torch.int16), ref8.view(torch.int16)), f"mxfp8 replay {rep}"
