@@ -124,6 +124,9 @@ int dispatch(const char *fn, tgemm::Problem p) {
     return fail(TGEMM_EINVAL, "%s: no %dx%d tile for this entry point (set by tgemm_set_tile)", fn, p.tile_m,
                 p.tile_n);
   hipError_t e = tgemm::launch(p);
+  if (e == hipErrorInvalidConfiguration)
+    return fail(TGEMM_ETOOBIG, "%s: a %lld x %lld output takes more tiles than one dispatch holds (2^24 workgroups)",
+                fn, (long long)p.M, (long long)p.N);
   if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   return TGEMM_OK;
 }

@@ -1164,7 +1164,10 @@ template <class T, int TM, int TN>
 hipError_t launch_shape(const Problem &p, Args a) {
   a.tiles_m = (int)((p.M + TM - 1) / TM);
   a.tiles_n = (int)((p.N + TN - 1) / TN);
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  // A dispatch holds fewer than 2^32 work-items per dimension.
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  if (tiles > (int64_t)(UINT32_MAX / kThreads)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)tiles), block(kThreads);
   hipLaunchKernelGGL((gemm_kernel<T, TM, TN>), grid, block, 0, p.stream, a);
   return hipGetLastError();
 }

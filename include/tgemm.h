@@ -20,7 +20,9 @@
  *   TGEMM_EALIGN     -2   a pointer not 16-byte aligned, or a size that
  *                         breaks the vector width (see each entry point)
  *   TGEMM_ETOOBIG    -3   an operand larger than the kernels' 32-bit
- *                         buffer offsets can address (see each entry point)
+ *                         buffer offsets can address (see each entry point),
+ *                         or an output of more tiles than one dispatch
+ *                         holds (2^24 workgroups of 256 work-items)
  *   TGEMM_EHIP       -4   no usable gfx950 device, or a HIP error at
  *                         initialisation or launch
  * After a non-zero return, tgemm_last_error() describes the failure.
