@@ -486,3 +486,53 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(c16.view(torch.int16), ref16.view(torch.int16)), f"bf16 replay {rep}"
         assert torch.equal(c8.view(torch.int16), ref8.view(torch.int16)), f"mxfp8 replay {rep}"
+
+
+def test_host_threads_keep_their_own_tile_and_error():
+    # tgemm_set_tile and the last-error message are per host thread: a
+    # thread that forces a tile the NN entry point lacks gets an error,
+    # while another thread's calls, with the automatic choice, run and see
+    # no message.  Both threads launch on streams of their own.
+    import threading
+    M, N, K = 320, 264, 520
+    x = workloads.make_random("f16_nn", M, N, K, seed=13)
+    a, b = to_dev(x["A"], "f16"), to_dev(x["B"], "f16")
+    torch.cuda.synchronize()
+    out = {}
+
+    def forced():
+        try:
+            tg.set_tile(256, 192)
+            with pytest.raises(tg.TgemmError, match="256x192"):
+                tg.gemm_f16_nn(a, b, stream=torch.cuda.Stream())
+            out["forced"] = tg.last_error()
+        except BaseException as e:  # reported by the main thread
+            out["forced_exc"] = e
+        finally:
+            tg.set_tile(0, 0)
+
+    def auto():
+        try:
+            s = torch.cuda.Stream()
+            cs = [tg.gemm_f16_nn(a, b, stream=s) for _ in range(20)]
+            s.synchronize()
+            out["auto"] = (cs, tg.last_error())
+        except BaseException as e:
+            out["auto_exc"] = e
+
+    print(f"[gpu] two host threads, f16_nn M={M} N={N} K={K}", flush=True)
+    threads = [threading.Thread(target=forced), threading.Thread(target=auto)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    for k in ("forced_exc", "auto_exc"):
+        if k in out:
+            raise out[k]
+    assert "256x192" in out["forced"]
+    cs, msg = out["auto"]
+    assert msg == ""
+    ref = oracle_full("f16_nn", x)
+    for c in cs:
+        assert_close("f16_nn", to_bits(c), ref, "thread")
