@@ -799,7 +799,12 @@ struct Kernel {
   template <int S, int JB, bool FIRST, int Q>
   __device__ __forceinline__ void mfma_one(int kt, Frags &f0, Frags &f1) {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
-    constexpr int H = q % kHalves, I = q / kHalves / kNBm, J = q / kHalves % kNBm;
+    // The 16-bit kinds snake through the y blocks (forward under even x
+    // blocks, backward under odd ones), so the two MFMAs at each turn share
+    // their y operand: less operand switching, 0.4% faster under the power
+    // cap at 4096 x 4096 x 8192.
+    constexpr int H = q % kHalves, I = q / kHalves / kNBm, J0 = q / kHalves % kNBm;
+    constexpr int J = !T::kScaled && (I & 1) ? kNBm - 1 - J0 : J0;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
     if constexpr (kFreeAt < kBarrierAt && Q == kFreeAt) {
       // Every wave's reads of this slot are done: its loads may start.
