@@ -789,7 +789,8 @@ struct Kernel {
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
-  // inside it x block q / kNBm times y block q % kNBm.  Interleaved with it:
+  // inside it x block q / kNBm times y block q % kNBm (16-bit kinds: in
+  // reverse order under odd x blocks).  Interleaved with it:
   //  * Q < kNR: read Q of substep 1 of this slot into f1;
   //  * before Q = kBarrierAt: wait for this wave's loads of slice kt + 1 and
   //    synchronise the workgroup (slot kt % kNS is then free);
