@@ -789,8 +789,8 @@ struct Kernel {
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
-  // inside it x block q / kNBm times y block q % kNBm (16-bit kinds: in
-  // reverse order under odd x blocks).  Interleaved with it:
+  // inside it x block q / kNBm times y block q % kNBm (in reverse order
+  // under odd x blocks).  Interleaved with it:
   //  * Q < kNR: read Q of substep 1 of this slot into f1;
   //  * before Q = kBarrierAt: wait for this wave's loads of slice kt + 1 and
   //    synchronise the workgroup (slot kt % kNS is then free);
@@ -800,12 +800,12 @@ struct Kernel {
   template <int S, int JB, bool FIRST, int Q>
   __device__ __forceinline__ void mfma_one(int kt, Frags &f0, Frags &f1) {
     constexpr int SUB = Q / kPerSub, q = Q % kPerSub;
-    // The 16-bit kinds snake through the y blocks (forward under even x
-    // blocks, backward under odd ones), so the two MFMAs at each turn share
-    // their y operand: less operand switching, 0.4% faster under the power
-    // cap at 4096 x 4096 x 8192.
+    // The y blocks snake (forward under even x blocks, backward under odd
+    // ones), so the two MFMAs at each turn share their y operand: less
+    // operand switching, 0.4% faster under the power cap at 4096 x 4096 x
+    // 8192 bf16, 0.2-0.9% for the block-scaled kinds.
     constexpr int H = q % kHalves, I = q / kHalves / kNBm, J0 = q / kHalves % kNBm;
-    constexpr int J = !T::kScaled && (I & 1) ? kNBm - 1 - J0 : J0;
+    constexpr int J = (I & 1) ? kNBm - 1 - J0 : J0;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
     if constexpr (kFreeAt < kBarrierAt && Q == kFreeAt) {
       // Every wave's reads of this slot are done: its loads may start.
