@@ -555,6 +555,24 @@ struct Kernel {
     }
     return r;
   }
+  // Half t of the same fragment (K values 4 t .. 4 t + 3 of each lane's
+  // eight): one transpose read into registers 2 t and 2 t + 1 of r.  (The
+  // both-K-major kernels read whole fragments through read_cols: written
+  // as two calls of this, that made their register allocation spill.)
+  template <int W>
+  __device__ __forceinline__ void read_cols_half(const LDS_AS uint8_t *slot, int col0, int sub, int t, Frag &r) const {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const int n = col0 + 4 * q;
+    const int kr = 32 * sub + 8 * g + 4 * t + e;
+    // (Masked to the slot so the compiler can see the read stays inside it
+    // and needs no wait for loads into the other slot.)
+    const int off = (kr * (2 * W) + (((n >> 3) ^ swz_nn<W>(kr)) << 4) + (n & 7) * 2) & (W * kRowBytes - 1);
+    const LDS_AS uint8_t *p = slot + off;
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)p);
+    u32x2 w = __builtin_bit_cast(u32x2, v);
+    r[2 * t] = w[0];
+    r[2 * t + 1] = w[1];
+  }
 
   // FIRST: the first K substep, whose MFMAs start from an accumulator of 0
   // (an inline constant), so the accumulators are never written by VALU code.
@@ -628,6 +646,38 @@ struct Kernel {
         f.y[R - kNBn] = read_rows(slots.a[S], wave_m * kWM + (R - kNBn) * kBlk, sub);
       else
         f.y[R - kNBn] = read_cols<TM>(slots.a[S], wave_m * kWM + (R - kNBn) * kBlk, sub);
+    }
+  }
+
+  // Read pieces.  With exactly one K-major operand its fragments are read
+  // as two pieces (the two transpose reads), each at an MFMA of its own, so
+  // the reads of a substep spread over twice as many MFMAs: 3-4% fewer
+  // cycles at 4096 x 4096 x 8192 (0.3-0.9% of the time under the power
+  // cap).  With both operands K-major the split made the kernel spill, and
+  // it stays off there.
+  static constexpr int kPx = T::kBK ? 1 : 2, kPy = T::kAK ? 1 : 2;
+  static constexpr int kPieces = kNBn * kPx + kNBm * kPy;
+  static constexpr bool kSplit =
+      !T::kScaled && (kPx == 2) != (kPy == 2) && kPieces <= kBarrierAt && kBarrierAt + kPieces <= kMfma;
+  static constexpr int kNRead = kSplit ? kPieces : kNR;  // read positions per substep
+
+  // Read piece P of substep `sub` of slot S (read R = P when not split).
+  template <int S, int P>
+  __device__ __forceinline__ void read_piece(Frags &f, int sub) const {
+    if constexpr (!kSplit) {
+      read_one<S, P>(f, sub);
+    } else if constexpr (P < kNBn * kPx) {
+      constexpr int R = P / kPx, t = P % kPx;
+      if constexpr (kPx == 1)
+        f.x[R] = read_rows(slots.b[S], wave_n * kWN + R * kBlk, sub);
+      else
+        read_cols_half<TN>(slots.b[S], wave_n * kWN + R * kBlk, sub, t, f.x[R]);
+    } else {
+      constexpr int R = (P - kNBn * kPx) / kPy, t = (P - kNBn * kPx) % kPy;
+      if constexpr (kPy == 1)
+        f.y[R] = read_rows(slots.a[S], wave_m * kWM + R * kBlk, sub);
+      else
+        read_cols_half<TM>(slots.a[S], wave_m * kWM + R * kBlk, sub, t, f.y[R]);
     }
   }
 
@@ -791,7 +841,7 @@ struct Kernel {
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
   // inside it x block q / kNBm times y block q % kNBm (in reverse order
   // under odd x blocks).  Interleaved with it:
-  //  * Q < kNR: read Q of substep 1 of this slot into f1;
+  //  * Q < kNRead: read piece Q of substep 1 of this slot into f1;
   //  * before Q = kBarrierAt: wait for this wave's loads of slice kt + 1 and
   //    synchronise the workgroup (slot kt % kNS is then free);
   //  * from kBarrierAt: reads of substep 0 of slice kt + 1 into f0;
@@ -830,8 +880,8 @@ struct Kernel {
       if constexpr (T::kFp6) convert_scales6<(S + 1) % 3>(kt + 1);
       if constexpr (T::kDt == kFp4) convert_scales4<(JB & 1) == 0, JB == 1 || JB == 2 ? 0 : 1, (JB + 1) & 1>(kt + 1);
     }
-    if constexpr (Q < kNR) read_one<S, Q>(f1, 1);
-    if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNR) read_one<(S + 1) % kNS, Q - kBarrierAt>(f0, 0);
+    if constexpr (Q < kNRead) read_piece<S, Q>(f1, 1);
+    if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNRead) read_piece<(S + 1) % kNS, Q - kBarrierAt>(f0, 0);
     if constexpr (kHead >= 0) load_one<(S + kNS - 1) % kNS>(kt + kNS - 1, kHead);
     if constexpr (kTail >= 0) load_one<S>(kt + kNS, kTail);
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
