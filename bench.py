@@ -1,30 +1,49 @@
 #!/usr/bin/env python3
 """Throughput of the tiled dense GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R]
+                    [--settle-s S] [--flush] [--workload NAME]
 
 A step is one C = A . B^T launch through the C ABI (gemm_bf16_nt) on the
-bf16 NT 4096 x 4096 x 8192 workload, inputs already resident in HBM.
-W untimed steps, then K timed steps between two synchronisations; the
-throughput is 2 M N K K / t (the pages' TFLOPS formula, TileLang SM100
-README, "Compilation and Usage").  Prints ONE JSON line on stdout; context
-goes to stderr.
+bf16 NT 4096 x 4096 x 8192 workload, inputs already resident in HBM.  The
+throughput of a region of K launches is 2 M N K K / t (the pages' TFLOPS
+formula, TileLang SM100 README, "Compilation and Usage").  Prints ONE JSON
+line on stdout; context goes to stderr.
 
-The line carries:
-  roofline     the kernel against MI355X's dense bf16 MFMA peak: algorithmic
-               flops per launch over the kernel's mean duration, taken from
-               the HIP events that bracket the timed region on the stream the
-               kernel runs on (one kernel per step, launched back to back);
-               `traffic` is the HBM bytes per launch from rocprofv3
+Timing, in this order, all on one non-default stream:
+  1. W untimed launches, then a first timed region of K launches: what a
+     short run measures, at whatever clock the chip has just after start
+     (reported under timing.first_region);
+  2. a settle phase: untimed launches for S seconds (default 2; the count
+     and the seconds are in the line).  Under sustained load the board
+     holds its power limit and the shader clock settles over about a second;
+  3. R timed regions of exactly K back-to-back launches, each between two
+     HIP events recorded on the launch stream.  `value` and `ms_per_step`
+     are the median region's; min and max are reported beside it.  With one
+     kernel per launch and the launches back to back, the median region's
+     time per launch is the kernel's mean duration that
+     `roofline.achieved` divides the algorithmic flops by (a rocprofv3
+     kernel trace of the same command gives the same mean within 1%);
+  4. K more launches, each between its own pair of events, for the spread
+     of single launches (min, median, max; the events' markers add a few us
+     to each, so these are not used for the mean).
+A clock probe (the library's tgemm_clock_probe: s_memtime against
+s_memrealtime over a 10 us spin on every XCD) runs right after the first
+region, after the settle phase and after the last timed region.
+
+--flush is the cold-cache variant: before every launch a 512 MB buffer is
+written, which evicts the inputs from the L2s and the 256 MB Infinity
+Cache; each region is followed by the same region of flushes alone, whose
+time is subtracted.
+
+The line also carries:
+  roofline     `traffic` is the HBM bytes per launch from rocprofv3
                FETCH_SIZE/WRITE_SIZE counters, calibrated on a plain copy,
                when a committed measurement matches the current kernel
                source, else null;
   cpu_baseline the CPU oracle (binary64 triple loop, all host threads) timed
                on a bounded sample of the same workload: whole rows of C,
                scaled to TFLOPS.
-
-The MI355X holds its board power cap under this load and its clock settles
-over about a second, so the default warmup is long (about 2 s of launches).
 
 Two helper modes serve the traffic measurement:
   --copy-calibration       only run a plain device-to-device copy of 1 GiB
@@ -352,11 +371,132 @@ def bench_quantize(args, w):
     print(json.dumps(line), flush=True)
 
 
+class ClockProbe:
+    """The shader clock per XCD, from the library's clock probe
+    (tgemm_clock_probe): each probe measures every XCD's clock over a 10 us
+    spin inside one kernel, so a probe enqueued right after a timed region
+    gives the clock the region ended at.  Two probes also give the average
+    clock between them from the counters' differences; that is reliable
+    only over long windows (the shader-clock counter is not continuous
+    across clock changes, so differences over a few ms can be far off)."""
+
+    def __init__(self):
+        import ctypes
+        import torch
+        self.buf = torch.zeros((2, 32), dtype=torch.int64, device="cuda")
+        self.khz = ctypes.c_int(0)
+
+    def sample(self, slot: int, stream) -> None:
+        import ctypes
+        import dense_tiled_gemm_bf16_amd as tg
+        tg.check(tg.lib().tgemm_clock_probe(ctypes.c_void_p(self.buf[slot].data_ptr()), ctypes.byref(self.khz),
+                                            ctypes.c_void_p(stream.cuda_stream)))
+
+    def _records(self, slot):
+        b = self.buf[slot].cpu().numpy().reshape(8, 4)
+        out = {}
+        for rec in b:
+            out.setdefault(int(rec[0]), [int(v) for v in rec[1:]])
+        return out
+
+    def spin_ghz(self, slot: int) -> dict:
+        """{xcd: GHz} measured inside the probe in `slot` (after a synchronisation)."""
+        rate = self.khz.value * 1e3
+        out = {}
+        for x, (_, _, spin) in self._records(slot).items():
+            dt, dr = spin & 0xFFFFFFFF, spin >> 32
+            if dr > 0 and rate > 0:
+                out[x] = dt / (dr / rate) / 1e9
+        return dict(sorted(out.items()))
+
+    def delta_ghz(self) -> dict:
+        """{xcd: GHz} averaged between the probes in slots 0 and 1."""
+        rate = self.khz.value * 1e3
+        r0, r1 = self._records(0), self._records(1)
+        out = {}
+        for x, (t0, c0, _) in r0.items():
+            if x in r1 and rate > 0 and r1[x][1] > c0:
+                out[x] = (r1[x][0] - t0) / ((r1[x][1] - c0) / rate) / 1e9
+        return dict(sorted(out.items()))
+
+
+def timed_region(launch, stream, steps: int, between=None):
+    """`steps` launches back to back on `stream` between two HIP events
+    recorded on that stream; `between` runs before each launch (inside the
+    region: only the flush variant uses it, and takes its time from
+    launch_spread instead).  Returns (region ms, host wall s)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            if between is not None:
+                between()
+            launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), time.perf_counter() - wall0
+
+
+def launch_spread(launch, stream, steps: int, between=None):
+    """`steps` launches, each between its own pair of HIP events on `stream`
+    (`between` outside the pairs).  Returns the per-launch times in us.  Each
+    event adds a marker to the stream, so these times include that overhead
+    (a few us against the kernel trace); they give the spread, not the mean."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            if between is not None:
+                between()
+            ev[2 * i].record(stream)
+            launch()
+            ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps)]
+
+
+def settle(launch, stream, seconds: float, kernel_us: float):
+    """Launch in batches of about 20 ms, synchronising after each, until
+    `seconds` of host time have passed (no timing).  Returns (launches, s)."""
+    import torch
+    batch = max(1, int(20e3 / max(kernel_us, 1.0)))
+    n, t0 = 0, time.perf_counter()
+    while seconds > 0 and time.perf_counter() - t0 < seconds:
+        with torch.cuda.stream(stream):
+            for _ in range(batch):
+                launch()
+        torch.cuda.synchronize()
+        n += batch
+    return n, time.perf_counter() - t0
+
+
+def _stats(v):
+    import statistics
+    return {"mean": round(statistics.fmean(v), 3), "median": round(statistics.median(v), 3),
+            "min": round(min(v), 3), "max": round(max(v), 3), "n": len(v)}
+
+
+def _mean_ghz(d):
+    return round(sum(d.values()) / len(d), 4) if d else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10000)
-    ap.add_argument("--warmup", type=int, default=10000)
+    ap.add_argument("--steps", type=int, default=1000, help="launches per timed region")
+    ap.add_argument("--warmup", type=int, default=50, help="untimed launches before the first timed region")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed regions of --steps launches after the settle phase; value = their median")
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of untimed launches between the cold region and the repeats, for the "
+                         "power-limited clock to settle (recorded in the line; 0 disables)")
+    ap.add_argument("--flush", action="store_true",
+                    help="cold-cache variant: write a 512 MB buffer before every launch (outside the "
+                         "launch's event pair); value from the per-launch kernel times")
     ap.add_argument("--workload", default="bf16_nt_4096x4096x8192")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work for the oracle baseline (0 disables it)")
@@ -374,6 +514,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; --gpus must be 1 "
               "(the GEMM has no multi-GPU path to measure)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.repeats < 1:
+        print("bench.py: --steps and --repeats must be >= 1, --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -402,36 +545,79 @@ def main():
     out = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
     stream = torch.cuda.Stream()
     launch = launcher(w, dev, out, stream)
-    torch.cuda.synchronize()
+    probe = ClockProbe()
+    between = None
+    if args.flush:
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        fills = [0]
 
+        def between():
+            fills[0] += 1
+            flush_buf.fill_(fills[0] & 255)
+    torch.cuda.synchronize()
+    peak = PEAK_TFLOPS[prec]
+    tfl = lambda us: w.flops / (us / 1e6) / 1e12
+
+    # 1. The untimed warmup launches, then the first timed region: exactly
+    #    the launches a short run makes, at whatever clock the chip has then.
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
+            if between is not None:
+                between()
             launch()
     torch.cuda.synchronize()
-
-    # Timed region: K back-to-back launches.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
+    c_ms, _ = timed_region(launch, stream, args.steps, between)
     with torch.cuda.stream(stream):
-        t_start.record(stream)
-        for _ in range(args.steps):
-            launch()
-        t_end.record(stream)
+        probe.sample(0, stream)
+    if between is not None:
+        c_ms -= timed_region(lambda: None, stream, args.steps, between)[0]
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    tflops = w.flops * args.steps / (total_ms / 1e3) / 1e12
+    c_ghz = probe.spin_ghz(0)
+    cold = {"warmup": args.warmup, "steps": args.steps, "ms_per_step": round(c_ms / args.steps, 5),
+            "tflops": round(w.flops * args.steps / (c_ms / 1e3) / 1e12, 2), "clock_ghz_at_end": _mean_ghz(c_ghz)}
+    log(f"[bench] first region ({args.warmup} warmup + {args.steps} timed launches): {cold['tflops']:.1f} TFLOPS, "
+        f"{c_ms / args.steps * 1e3:.1f} us/launch, clock at its end {cold['clock_ghz_at_end']} GHz")
 
-    # One kernel per step, launched back to back on `stream`: the kernel's
-    # mean duration is the event-timed region over the step count.
-    kernel_ms = ms_per_step
-    achieved = w.flops / (kernel_ms / 1e3) / 1e12
-    peak = PEAK_TFLOPS[prec]
-    log(f"[bench] {args.steps} steps in {total_ms:.3f} ms (wall {wall*1e3:.1f} ms): "
-        f"{ms_per_step*1e3:.1f} us/step, {tflops:.1f} TFLOPS = {100*tflops/peak:.1f}% of {peak}")
+    # 2. Untimed launches until the power-limited clock has settled.
+    n_settle, s_settle = settle(launch if between is None else (lambda: (between(), launch())), stream,
+                                args.settle_s, c_ms / args.steps * 1e3)
+    with torch.cuda.stream(stream):
+        probe.sample(1, stream)
+    torch.cuda.synchronize()
+    settle_ghz, settle_avg = probe.spin_ghz(1), probe.delta_ghz()
+    log(f"[bench] settle: {n_settle} launches in {s_settle:.2f} s; clock at its end {_mean_ghz(settle_ghz)} GHz, "
+        f"average over it {_mean_ghz(settle_avg)} GHz")
+
+    # 3. The timed regions: `repeats` regions of exactly `steps` launches.
+    regions = []
+    for r in range(args.repeats):
+        ms, wall = timed_region(launch, stream, args.steps, between)
+        if between is not None:
+            # Flush variant: the same region with the flushes alone, right
+            # after; the difference is the launches' own time.
+            fl_ms, _ = timed_region(lambda: None, stream, args.steps, between)
+            ms -= fl_ms
+        regions.append({"ms": ms, "wall_s": wall, "tflops": w.flops * args.steps / (ms / 1e3) / 1e12})
+        log(f"[bench] region {r}: {args.steps} launches in {ms:.3f} ms (wall {wall*1e3:.1f} ms): "
+            f"{regions[-1]['tflops']:.1f} TFLOPS, {ms / args.steps * 1e3:.2f} us/launch")
+    with torch.cuda.stream(stream):
+        probe.sample(0, stream)
+    torch.cuda.synchronize()
+    rep_ghz = probe.spin_ghz(0)
+
+    # 4. The spread of single launches (event pair around each).
+    spread = _stats(launch_spread(launch, stream, args.steps, between))
+
+    order = sorted(range(len(regions)), key=lambda i: regions[i]["tflops"])
+    med = regions[order[len(order) // 2]]
+    tflops = med["tflops"]
+    ms_per_step = med["ms"] / args.steps
+    kernel_us = ms_per_step * 1e3
+    achieved = tfl(kernel_us)
+    log(f"[bench] median region: {tflops:.1f} TFLOPS = {100*tflops/peak:.1f}% of {peak}; kernel "
+        f"{kernel_us:.2f} us -> {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}%; clock at the end of the "
+        f"regions {_mean_ghz(rep_ghz)} GHz; single launches (event pair each) median {spread['median']:.2f} us, "
+        f"min {spread['min']:.2f}, max {spread['max']:.2f}")
 
     parity = None if args.no_parity else parity_sample(w, x, out)
     if parity is not None:
@@ -444,9 +630,12 @@ def main():
         log(f"[bench] cpu oracle: {cpu['value']*1e3:.3f} GFLOPS on {cpu['cores']} threads ({cpu['sample']})")
         cpu.pop("seconds", None)
 
-    traffic = measured_traffic(w.name)
+    traffic = None if args.flush else measured_traffic(w.name)
+    metric = METRIC if w.name == "bf16_nt_4096x4096x8192" else f"TFLOPS (2MNK/t), {w.description}, 1 GPU"
+    if args.flush:
+        metric += ", cold cache (512 MB written before each launch, the flushes' own time subtracted)"
     line = {
-        "metric": METRIC if w.name == "bf16_nt_4096x4096x8192" else f"TFLOPS (2MNK/t), {w.description}, 1 GPU",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -466,8 +655,31 @@ def main():
                    "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel_mean_us": round(kernel_ms * 1e3, 2),
-                     "flops_per_launch": w.flops},
+                     "kernel_mean_us": round(kernel_us, 3), "flops_per_launch": w.flops,
+                     "kernel_time_source": "median timed region: two HIP events on the launch stream around "
+                                           f"{args.steps} back-to-back launches, one kernel per launch" +
+                                           (", less the same region of flushes alone" if args.flush else "")},
+        "timing": {
+            "repeats": args.repeats,
+            "region_tflops": {"median": round(med["tflops"], 2),
+                              "min": round(regions[order[0]]["tflops"], 2),
+                              "max": round(regions[order[-1]]["tflops"], 2)},
+            "single_launch_us": dict(spread, note="an event pair around each launch; the markers add a few us "
+                                                  "to each"),
+            "clock_ghz": {"end_of_first_region": _mean_ghz(c_ghz), "end_of_settle": _mean_ghz(settle_ghz),
+                          "average_over_settle": _mean_ghz(settle_avg),
+                          "end_of_timed_regions": _mean_ghz(rep_ghz),
+                          "per_xcd_end_of_timed_regions": {str(k): round(v, 4) for k, v in rep_ghz.items()},
+                          "source": "tgemm_clock_probe right after the first region, the settle phase and the "
+                                    "last timed region: s_memtime against s_memrealtime over a 10 us spin on "
+                                    "every XCD, mean over the XCDs; the settle average from the counters' "
+                                    "differences across it"},
+            "settle": {"seconds": round(s_settle, 2), "launches": n_settle,
+                       "why": "untimed launches between the first region and the timed regions; under sustained "
+                              "load the board holds its power limit and the clock settles over about a second"},
+            "first_region": cold,
+            "flush": bool(args.flush),
+        },
         "cpu_baseline": cpu,
         "parity": parity,
     }

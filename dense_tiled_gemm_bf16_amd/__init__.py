@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64, p]
         f.restype = ctypes.c_int
     L.quantize_mxfp8.restype = ctypes.c_int
+    L.tgemm_clock_probe.argtypes = [p, ctypes.POINTER(ctypes.c_int), p]
+    L.tgemm_clock_probe.restype = ctypes.c_int
     _lib = L
     return L
 

@@ -281,6 +281,25 @@ int quantize_mxfp8(int64_t M, int64_t K, const float *x, void *q, void *scales, 
   return TGEMM_OK;
 }
 
+int tgemm_clock_probe(void *out, int *wallclock_khz, hipStream_t stream) {
+  static const char fn[] = "tgemm_clock_probe";
+  g_err[0] = '\0';
+  if (!out) return fail(TGEMM_EINVAL, "%s: out is NULL", fn);
+  if (misaligned(out)) return fail(TGEMM_EALIGN, "%s: out is not 16-byte aligned", fn);
+  int rc = ensure_device();
+  if (rc != TGEMM_OK) return rc;
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: wall-clock rate: %s", fn, hipGetErrorString(e));
+  if (khz <= 0) return fail(TGEMM_EHIP, "%s: the device reports no constant-rate counter", fn);
+  if (wallclock_khz) *wallclock_khz = khz;
+  // A spin of 10 us of constant-rate ticks.
+  e = tgemm::launch_clock_probe(out, (uint32_t)(khz / 100 > 0 ? khz / 100 : 1), stream);
+  if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return TGEMM_OK;
+}
+
 int tgemm_set_tile(int tile_m, int tile_n) {
   g_err[0] = '\0';
   const bool known = (tile_m == 0 && tile_n == 0) || (tile_m == 256 && tile_n == 256) ||

@@ -53,4 +53,13 @@ struct QuantProblem {
 // Enqueues the quantiser for `p` on p.stream.  Returns the launch status.
 hipError_t launch_quantize(const QuantProblem &p);
 
+// Workgroups of the clock probe: one per XCD (8 on MI355X), in turn.
+constexpr int kProbeGroups = 8;
+
+// Enqueues the clock probe on `stream`: writes kProbeGroups records of four
+// uint64 {XCC id, s_memtime, s_memrealtime, spin} to the device buffer `out`,
+// spin = (constant-rate ticks << 32) | shader-clock ticks over a spin of
+// `ticks` constant-rate ticks.
+hipError_t launch_clock_probe(void *out, uint32_t ticks, hipStream_t stream);
+
 }  // namespace tgemm

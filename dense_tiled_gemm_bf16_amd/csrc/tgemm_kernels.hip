@@ -1223,9 +1223,11 @@ hipError_t launch_shape(const Problem &p, Args a) {
   // A dispatch holds fewer than 2^32 work-items per dimension.
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   if (tiles > (int64_t)(UINT32_MAX / kThreads)) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)tiles), block(kThreads);
-  hipLaunchKernelGGL((gemm_kernel<T, TM, TN>), grid, block, 0, p.stream, a);
-  return hipGetLastError();
+  // hipLaunchKernel returns this launch's own status (hipGetLastError could
+  // report an earlier, unrelated failure of the calling thread).
+  void *args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, TM, TN>), dim3((unsigned)tiles),
+                         dim3(kThreads), args, 0, p.stream);
 }
 
 // The 16-bit kernels of one operand layout, by tile shape (256 x 192 only

@@ -110,8 +110,9 @@ hipError_t launch_quantize(const QuantProblem &p) {
   a.segs = p.M * a.segs_per_row;
   const int64_t wgs = (a.segs + kSegsPerWg - 1) / kSegsPerWg;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)wgs), dim3(kQThreads), 0, p.stream, a);
-  return hipGetLastError();
+  void *args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&quantize_mxfp8_kernel), dim3((unsigned)wgs),
+                         dim3(kQThreads), args, 0, p.stream);
 }
 
 }  // namespace tgemm

@@ -251,8 +251,38 @@ TGEMM_API int tgemm_init(void);
 /*
  * Message for the last failing call on this host thread; "" after a
  * successful call.  The pointer stays valid until the thread's next call.
+ * This is the get_last_error() of the host wrapper on the velog "tilelang"
+ * page (1.3 Code Generation & Runtime), which keeps the message of the last
+ * failure in a static buffer; here the buffer is per host thread (1024
+ * bytes, the page's size) and is cleared by every call.
  */
 TGEMM_API const char *tgemm_last_error(void);
+
+/*
+ * Shader-clock probe, a measurement helper off the GEMM path.  The pages
+ * time a kernel and report TFLOPS = 2 M N K / t (TileLang SM100 README,
+ * "Compilation and Usage"); on MI355X that time also depends on the shader
+ * clock the board's power limit allows.  Each of the probe's workgroups
+ * reads its XCD's shader-clock counter (s_memtime) and constant-rate counter
+ * (s_memrealtime), spins for 10 us of constant-rate ticks and reads both
+ * again; the ratio of the two differences times the constant rate is that
+ * XCD's clock at that moment.  Enqueued right after a timed region, it gives
+ * the clock the region ended at.
+ *
+ *   out            device pointer to 32 uint64 (256 bytes), 16-byte
+ *                  aligned, owned by the caller; written on `stream` with 8
+ *                  records, one per workgroup (the workgroups go to the XCDs
+ *                  in turn): {XCC id, shader-clock count and constant-rate
+ *                  count at the start of the spin, spin}, where spin holds
+ *                  the constant-rate ticks of the spin in its upper 32 bits
+ *                  and the shader-clock ticks in its lower 32 bits
+ *   wallclock_khz  host pointer, may be NULL; receives the constant-rate
+ *                  counter's frequency in kHz (written before returning)
+ *
+ * Returns TGEMM_OK, TGEMM_EINVAL (out NULL), TGEMM_EALIGN (out misaligned)
+ * or TGEMM_EHIP.
+ */
+TGEMM_API int tgemm_clock_probe(void *out, int *wallclock_khz, hipStream_t stream);
 
 /*
  * Output tile override for the calling host thread's later calls, for

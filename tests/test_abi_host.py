@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
         ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_mxfp4_nt", "gemm_mxfp6_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
-         "tgemm_last_error", "tgemm_set_tile"])
+         "tgemm_last_error", "tgemm_set_tile", "tgemm_clock_probe"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -248,3 +248,12 @@ def test_wrapper_requires_one_device():
     assert tg._same_device(a=a, x=a) == torch.device("cpu")
     with pytest.raises(ValueError, match="b is on meta"):
         tg._same_device(a=a, b=b)
+
+
+def test_clock_probe_validation():
+    L = tg.lib()
+    khz = ctypes.c_int(0)
+    assert L.tgemm_clock_probe(None, ctypes.byref(khz), None) == tg.EINVAL
+    assert "out is NULL" in tg.last_error()
+    assert L.tgemm_clock_probe(A16 + 8, ctypes.byref(khz), None) == tg.EALIGN
+    assert "aligned" in tg.last_error()

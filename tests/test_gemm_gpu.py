@@ -6,8 +6,8 @@ README, "Compilation and Usage"), here against the binary64 oracle rounded
 once to the output type.  On integer-valued inputs every fp32 partial sum
 is exact, so there the GPU and the oracle must agree bit for bit.
 
-Small shapes are compared in full; the large workloads are compared on
-sampled outputs plus whole rows and columns computed one output at a time.
+Every workload is compared in full, at its real size, on random and on
+integer-valued inputs; only the maximum-size cases elsewhere are sampled.
 """
 import numpy as np
 import pytest
@@ -97,17 +97,6 @@ def assert_bitwise(got_bits, ref_bits, what=""):
                              f"want {ref_bits[diff][:8]}")
 
 
-def full_rows_cols(M, N, count=2000, seed=1):
-    """Sampled positions plus every output of a few whole rows and columns
-    (first, last, and tile edges)."""
-    rows, cols = workloads.sample_positions(M, N, count, seed)
-    r_full = sorted({0, min(255, M - 1), min(256, M - 1), M - 1})
-    c_full = sorted({0, min(255, N - 1), min(256, N - 1), N - 1})
-    rr = [rows] + [np.full(N, r) for r in r_full] + [np.arange(M) for _ in c_full]
-    cc = [cols] + [np.arange(N) for _ in r_full] + [np.full(M, c) for c in c_full]
-    return np.concatenate(rr).astype(np.int64), np.concatenate(cc).astype(np.int64)
-
-
 # --- the five workloads -----------------------------------------------------------
 
 SMALL = ["bf16_nt_256", "f16_nn_1024"]
@@ -122,26 +111,66 @@ def test_small_workload_full_parity(name):
     assert_close(w.kind, got, oracle_full(w.kind, x), name)
 
 
-@pytest.mark.parametrize("name", LARGE)
-def test_large_workload_sampled_parity(name):
-    w = workloads.WORKLOADS[name]
-    x = workloads.make_inputs(w)
-    got = to_bits(run(w.kind, x, w.M, w.N, w.K))
-    rows, cols = full_rows_cols(w.M, w.N)
-    assert_close(w.kind, got[rows, cols], oracle_at(w.kind, x, rows, cols), name)
-    assert np.isfinite(values(w.kind, got)).all()
-
-
-@pytest.mark.parametrize("name", SMALL + LARGE)
-def test_workload_integer_inputs_bitwise(name):
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workload_integer_inputs_bitwise(name):
+    """Integer-valued inputs: every fp32 partial sum is exact, so every output
+    must match the oracle bit for bit."""
     w = workloads.WORKLOADS[name]
     x = workloads.make_integer(w.kind, w.M, w.N, w.K, seed=5)
-    got = to_bits(run(w.kind, x, w.M, w.N, w.K))
-    if name in SMALL:
-        assert_bitwise(got, oracle_full(w.kind, x), name)
+    assert_bitwise(to_bits(run(w.kind, x, w.M, w.N, w.K)), oracle_full(w.kind, x), name)
+
+
+# The full-size workloads are compared output by output, in full.  The oracle
+# takes tens of seconds per workload on the host's cores, so each comparison
+# is split into bands of rows (a test each, sharing one GPU result).
+LARGE_BANDS = {"bf16_nt_4096x4096x8192": 2, "bf16_nt_4000x3000x5000": 1, "mxfp8_nt_4096": 4}
+LARGE_CASES = [(name, variant, band, LARGE_BANDS[name]) for name in LARGE for variant in ("random", "integer")
+               for band in range(LARGE_BANDS[name])]
+
+
+@pytest.fixture(scope="module")
+def large_result():
+    """(inputs, GPU output bits) of a full-size workload, random or integer
+    inputs; the last one is kept for the next band."""
+    cache = {}
+
+    def get(name, variant):
+        if (name, variant) not in cache:
+            cache.clear()
+            w = workloads.WORKLOADS[name]
+            x = workloads.make_inputs(w) if variant == "random" else workloads.make_integer(w.kind, w.M, w.N, w.K,
+                                                                                          seed=5)
+            cache[(name, variant)] = (x, to_bits(run(w.kind, x, w.M, w.N, w.K)))
+        return cache[(name, variant)]
+    return get
+
+
+def oracle_rows(kind, x, r0, r1):
+    """Rows r0 .. r1 - 1 of the oracle's C: the same function on that band of
+    A's rows (and their scales) with all of B."""
+    if kind == "bf16_nt":
+        return oracle.gemm_bf16_nt(x["A"][r0:r1], x["B"])
+    if kind == "f16_nn":
+        return oracle.gemm_f16_nn(x["A"][r0:r1], x["B"])
+    return oracle.gemm_mxfp8_nt(x["qA"][r0:r1], x["qB"], x["sA"][r0:r1], x["sB"])
+
+
+@pytest.mark.parametrize("name,variant,band,bands", LARGE_CASES,
+                         ids=[f"{n}-{v}-{b}of{nb}" for n, v, b, nb in LARGE_CASES])
+def test_large_workload_full_parity(large_result, name, variant, band, bands):
+    """Every output of the full-size workloads against the oracle: random
+    inputs within the tolerance, integer-valued inputs (exact fp32 sums) bit
+    for bit."""
+    w = workloads.WORKLOADS[name]
+    x, got = large_result(name, variant)
+    r0, r1 = band * w.M // bands, (band + 1) * w.M // bands
+    ref = oracle_rows(w.kind, x, r0, r1)
+    what = f"{name} {variant} rows {r0}..{r1 - 1}"
+    if variant == "random":
+        assert_close(w.kind, got[r0:r1], ref, what)
+        assert np.isfinite(values(w.kind, got[r0:r1])).all()
     else:
-        rows, cols = full_rows_cols(w.M, w.N)
-        assert_bitwise(got[rows, cols], oracle_at(w.kind, x, rows, cols), name)
+        assert_bitwise(got[r0:r1], ref, what)
 
 
 # --- tails, several tiles, degenerate shapes ------------------------------------------
