@@ -27,9 +27,14 @@ Timing, in this order, all on one non-default stream:
   4. K more launches, each between its own pair of events, for the spread
      of single launches (min, median, max; the events' markers add a few us
      to each, so these are not used for the mean).
-A clock probe (the library's tgemm_clock_probe: s_memtime against
-s_memrealtime over a 10 us spin on every XCD) runs right after the first
-region, after the settle phase and after the last timed region.
+Clock probes (the library's tgemm_clock_probe: s_memtime against
+s_memrealtime on every CU, paired per CU) bracket the first region, the
+settle phase and the set of timed regions, giving the shader clock each XCD
+delivered over each.
+
+--graph captures each region's K launches into a HIP graph once and times
+its replay, so that host launch costs do not enter the time of short
+kernels (the small workloads).
 
 --flush is the cold-cache variant: before every launch a 512 MB buffer is
 written, which evicts the inputs from the L2s and the 256 MB Infinity
@@ -128,12 +133,22 @@ def device_inputs(w, seed=0):
     return x, dev
 
 
-def launcher(w, dev, out, stream):
+def launcher(w, dev, out, stream, splitk=None):
+    import torch
     import dense_tiled_gemm_bf16_amd as tg
     L = tg.lib()
     s = stream.cuda_stream
     M, N, K = w.M, w.N, w.K
-    if w.kind == "bf16_nt":
+    if splitk is not None:
+        # The K-split entry point (16-bit kinds), its workspace allocated here.
+        need = L.tgemm_splitk_workspace_bytes(M, N, splitk)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        fn = L.gemm_bf16_splitk if w.kind == "bf16_nt" else L.gemm_f16_splitk
+        tb, ldb = (1, K) if w.kind == "bf16_nt" else (0, N)
+        args = (0, tb, M, N, K, dev["A"].data_ptr(), K, dev["B"].data_ptr(), ldb, out.data_ptr(), N, splitk,
+                ws.data_ptr(), ws.numel(), s)
+        dev["_ws"] = ws
+    elif w.kind == "bf16_nt":
         args = (M, N, K, dev["A"].data_ptr(), dev["B"].data_ptr(), out.data_ptr(), s)
         fn = L.gemm_bf16_nt
     elif w.kind == "f16_nn":
@@ -372,18 +387,18 @@ def bench_quantize(args, w):
 
 
 class ClockProbe:
-    """The shader clock per XCD, from the library's clock probe
-    (tgemm_clock_probe): each probe measures every XCD's clock over a 10 us
-    spin inside one kernel, so a probe enqueued right after a timed region
-    gives the clock the region ended at.  Two probes also give the average
-    clock between them from the counters' differences; that is reliable
-    only over long windows (the shader-clock counter is not continuous
-    across clock changes, so differences over a few ms can be far off)."""
+    """The shader clock delivered between two probes, per XCD: the library's
+    clock probe (tgemm_clock_probe) records, on every CU, that CU's
+    shader-clock counter and the constant-rate counter; each CU's pair of
+    records gives its average clock between the probes, and an XCD's is the
+    mean over its CUs (they agree to a few MHz within an XCD)."""
+
+    RECORDS = 256
 
     def __init__(self):
         import ctypes
         import torch
-        self.buf = torch.zeros((2, 32), dtype=torch.int64, device="cuda")
+        self.buf = torch.zeros((2, 4 * self.RECORDS), dtype=torch.int64, device="cuda")
         self.khz = ctypes.c_int(0)
 
     def sample(self, slot: int, stream) -> None:
@@ -393,48 +408,59 @@ class ClockProbe:
                                             ctypes.c_void_p(stream.cuda_stream)))
 
     def _records(self, slot):
-        b = self.buf[slot].cpu().numpy().reshape(8, 4)
+        """{(xcc, se/sh/cu bits): (shader-clock count, constant-rate count)}."""
+        b = self.buf[slot].cpu().numpy().reshape(self.RECORDS, 4)
         out = {}
         for rec in b:
-            out.setdefault(int(rec[0]), [int(v) for v in rec[1:]])
+            key = (int(rec[0]) >> 32, (int(rec[0]) >> 8) & 0xFF)
+            out.setdefault(key, (int(rec[1]), int(rec[2])))
         return out
 
-    def spin_ghz(self, slot: int) -> dict:
-        """{xcd: GHz} measured inside the probe in `slot` (after a synchronisation)."""
-        rate = self.khz.value * 1e3
-        out = {}
-        for x, (_, _, spin) in self._records(slot).items():
-            dt, dr = spin & 0xFFFFFFFF, spin >> 32
-            if dr > 0 and rate > 0:
-                out[x] = dt / (dr / rate) / 1e9
-        return dict(sorted(out.items()))
-
-    def delta_ghz(self) -> dict:
-        """{xcd: GHz} averaged between the probes in slots 0 and 1."""
+    def ghz(self) -> dict:
+        """{xcd: GHz} between the probes in slots 0 and 1 (after a synchronisation)."""
         rate = self.khz.value * 1e3
         r0, r1 = self._records(0), self._records(1)
-        out = {}
-        for x, (t0, c0, _) in r0.items():
-            if x in r1 and rate > 0 and r1[x][1] > c0:
-                out[x] = (r1[x][0] - t0) / ((r1[x][1] - c0) / rate) / 1e9
-        return dict(sorted(out.items()))
+        per = {}
+        for key, (t0, c0) in r0.items():
+            if key in r1 and rate > 0 and r1[key][1] > c0:
+                per.setdefault(key[0], []).append((r1[key][0] - t0) / ((r1[key][1] - c0) / rate) / 1e9)
+        return {x: sum(v) / len(v) for x, v in sorted(per.items())}
 
 
-def timed_region(launch, stream, steps: int, between=None):
+_graphs = {}
+
+
+def timed_region(launch, stream, steps: int, between=None, graph: bool = False):
     """`steps` launches back to back on `stream` between two HIP events
     recorded on that stream; `between` runs before each launch (inside the
-    region: only the flush variant uses it, and takes its time from
-    launch_spread instead).  Returns (region ms, host wall s)."""
+    region: the flush variant subtracts a region of flushes alone).  With
+    `graph`, the launches (and flushes) are captured once into a HIP graph
+    and the region replays it, so host launch costs do not enter the time.
+    Returns (region ms, host wall s)."""
     import torch
+
+    def body():
+        for _ in range(steps):
+            if between is not None:
+                between()
+            launch()
+
+    if graph:
+        key = (id(launch), id(between), steps)
+        if key not in _graphs:
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                body()
+            torch.cuda.synchronize()
+            _graphs[key] = g
+        body = _graphs[key].replay
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for _ in range(steps):
-            if between is not None:
-                between()
-            launch()
+        body()
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1), time.perf_counter() - wall0
@@ -504,6 +530,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--tile", default="auto",
                     help="output tile TMxTN (e.g. 256x192); default: the library's own choice")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each timed region's launches into a HIP graph once and time its replay "
+                         "(for kernels shorter than the host's launch cost)")
+    ap.add_argument("--splitk", type=int, default=None, metavar="S",
+                    help="16-bit workloads: call the K-split entry point with S splits (0: the library "
+                         "chooses); default: the plain entry point")
     ap.add_argument("--record-traffic", metavar="DIR")
     args = ap.parse_args()
 
@@ -544,8 +576,12 @@ def main():
     out_dtype = torch.float16 if w.kind == "f16_nn" else torch.bfloat16
     out = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
     stream = torch.cuda.Stream()
-    launch = launcher(w, dev, out, stream)
+    if args.splitk is not None and w.kind not in ("bf16_nt", "f16_nn"):
+        print("bench.py: --splitk is for the 16-bit workloads", file=sys.stderr)
+        sys.exit(2)
+    launch = launcher(w, dev, out, stream, args.splitk)
     probe = ClockProbe()
+    noop = lambda: None
     between = None
     if args.flush:
         flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -566,44 +602,50 @@ def main():
                 between()
             launch()
     torch.cuda.synchronize()
-    c_ms, _ = timed_region(launch, stream, args.steps, between)
     with torch.cuda.stream(stream):
         probe.sample(0, stream)
-    if between is not None:
-        c_ms -= timed_region(lambda: None, stream, args.steps, between)[0]
+    c_ms, _ = timed_region(launch, stream, args.steps, between, args.graph)
+    with torch.cuda.stream(stream):
+        probe.sample(1, stream)
     torch.cuda.synchronize()
-    c_ghz = probe.spin_ghz(0)
+    c_ghz = probe.ghz()
+    if between is not None:
+        c_ms -= timed_region(noop, stream, args.steps, between, args.graph)[0]
     cold = {"warmup": args.warmup, "steps": args.steps, "ms_per_step": round(c_ms / args.steps, 5),
-            "tflops": round(w.flops * args.steps / (c_ms / 1e3) / 1e12, 2), "clock_ghz_at_end": _mean_ghz(c_ghz)}
+            "tflops": round(w.flops * args.steps / (c_ms / 1e3) / 1e12, 2), "clock_ghz": _mean_ghz(c_ghz)}
     log(f"[bench] first region ({args.warmup} warmup + {args.steps} timed launches): {cold['tflops']:.1f} TFLOPS, "
-        f"{c_ms / args.steps * 1e3:.1f} us/launch, clock at its end {cold['clock_ghz_at_end']} GHz")
+        f"{c_ms / args.steps * 1e3:.1f} us/launch, clock {cold['clock_ghz']} GHz")
 
     # 2. Untimed launches until the power-limited clock has settled.
+    with torch.cuda.stream(stream):
+        probe.sample(0, stream)
     n_settle, s_settle = settle(launch if between is None else (lambda: (between(), launch())), stream,
                                 args.settle_s, c_ms / args.steps * 1e3)
     with torch.cuda.stream(stream):
         probe.sample(1, stream)
     torch.cuda.synchronize()
-    settle_ghz, settle_avg = probe.spin_ghz(1), probe.delta_ghz()
-    log(f"[bench] settle: {n_settle} launches in {s_settle:.2f} s; clock at its end {_mean_ghz(settle_ghz)} GHz, "
-        f"average over it {_mean_ghz(settle_avg)} GHz")
+    settle_ghz = probe.ghz()
+    log(f"[bench] settle: {n_settle} launches in {s_settle:.2f} s, clock {_mean_ghz(settle_ghz)} GHz")
 
-    # 3. The timed regions: `repeats` regions of exactly `steps` launches.
+    # 3. The timed regions: `repeats` regions of exactly `steps` launches,
+    #    bracketed together by one pair of clock probes.
     regions = []
+    with torch.cuda.stream(stream):
+        probe.sample(0, stream)
     for r in range(args.repeats):
-        ms, wall = timed_region(launch, stream, args.steps, between)
+        ms, wall = timed_region(launch, stream, args.steps, between, args.graph)
         if between is not None:
             # Flush variant: the same region with the flushes alone, right
             # after; the difference is the launches' own time.
-            fl_ms, _ = timed_region(lambda: None, stream, args.steps, between)
+            fl_ms, _ = timed_region(noop, stream, args.steps, between, args.graph)
             ms -= fl_ms
         regions.append({"ms": ms, "wall_s": wall, "tflops": w.flops * args.steps / (ms / 1e3) / 1e12})
         log(f"[bench] region {r}: {args.steps} launches in {ms:.3f} ms (wall {wall*1e3:.1f} ms): "
             f"{regions[-1]['tflops']:.1f} TFLOPS, {ms / args.steps * 1e3:.2f} us/launch")
     with torch.cuda.stream(stream):
-        probe.sample(0, stream)
+        probe.sample(1, stream)
     torch.cuda.synchronize()
-    rep_ghz = probe.spin_ghz(0)
+    rep_ghz = probe.ghz()
 
     # 4. The spread of single launches (event pair around each).
     spread = _stats(launch_spread(launch, stream, args.steps, between))
@@ -615,8 +657,8 @@ def main():
     kernel_us = ms_per_step * 1e3
     achieved = tfl(kernel_us)
     log(f"[bench] median region: {tflops:.1f} TFLOPS = {100*tflops/peak:.1f}% of {peak}; kernel "
-        f"{kernel_us:.2f} us -> {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}%; clock at the end of the "
-        f"regions {_mean_ghz(rep_ghz)} GHz; single launches (event pair each) median {spread['median']:.2f} us, "
+        f"{kernel_us:.2f} us -> {achieved:.1f} TFLOP/s = {100*achieved/peak:.1f}%; clock over the regions "
+        f"{_mean_ghz(rep_ghz)} GHz; single launches (event pair each) median {spread['median']:.2f} us, "
         f"min {spread['min']:.2f}, max {spread['max']:.2f}")
 
     parity = None if args.no_parity else parity_sample(w, x, out)
@@ -652,6 +694,8 @@ def main():
                    "layout": "NT" if w.kind != "f16_nn" else "NN",
                    "accumulate": "fp32",
                    "tile": (f"{tile[0]}x{tile[1]}" if tile else "auto") + ", 4 waves, 128-byte K slices",
+                   "entry": "gemm_bf16_splitk / gemm_f16_splitk, splits=%d" % args.splitk
+                            if args.splitk is not None else "plain",
                    "pct_of_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -666,19 +710,18 @@ def main():
                               "max": round(regions[order[-1]]["tflops"], 2)},
             "single_launch_us": dict(spread, note="an event pair around each launch; the markers add a few us "
                                                   "to each"),
-            "clock_ghz": {"end_of_first_region": _mean_ghz(c_ghz), "end_of_settle": _mean_ghz(settle_ghz),
-                          "average_over_settle": _mean_ghz(settle_avg),
-                          "end_of_timed_regions": _mean_ghz(rep_ghz),
-                          "per_xcd_end_of_timed_regions": {str(k): round(v, 4) for k, v in rep_ghz.items()},
-                          "source": "tgemm_clock_probe right after the first region, the settle phase and the "
-                                    "last timed region: s_memtime against s_memrealtime over a 10 us spin on "
-                                    "every XCD, mean over the XCDs; the settle average from the counters' "
-                                    "differences across it"},
+            "clock_ghz": {"timed_regions": _mean_ghz(rep_ghz), "settle": _mean_ghz(settle_ghz),
+                          "first_region": _mean_ghz(c_ghz),
+                          "per_xcd_timed_regions": {str(k): round(v, 4) for k, v in rep_ghz.items()},
+                          "source": "tgemm_clock_probe before and after the first region, the settle phase and "
+                                    "the set of timed regions (flushes included, if any): s_memtime against "
+                                    "s_memrealtime, paired per CU, mean over each XCD's CUs, then over the XCDs"},
             "settle": {"seconds": round(s_settle, 2), "launches": n_settle,
                        "why": "untimed launches between the first region and the timed regions; under sustained "
                               "load the board holds its power limit and the clock settles over about a second"},
             "first_region": cold,
             "flush": bool(args.flush),
+            "graph": bool(args.graph),
         },
         "cpu_baseline": cpu,
         "parity": parity,

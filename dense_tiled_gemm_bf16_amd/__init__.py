@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64, p]
         f.restype = ctypes.c_int
     L.quantize_mxfp8.restype = ctypes.c_int
+    for f in (L.gemm_bf16_splitk, L.gemm_f16_splitk):
+        f.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64, ctypes.c_int, p,
+                      ctypes.c_uint64, p]
+        f.restype = ctypes.c_int
+    L.tgemm_splitk_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+    L.tgemm_splitk_workspace_bytes.restype = ctypes.c_uint64
     L.tgemm_clock_probe.argtypes = [p, ctypes.POINTER(ctypes.c_int), p]
     L.tgemm_clock_probe.restype = ctypes.c_int
     _lib = L
@@ -244,6 +250,41 @@ def gemm(a, b, out=None, stream=None):
     dev = _same_device(a=a, b=b, out=out)
     fn = lib().gemm_bf16 if a.dtype == torch.bfloat16 else lib().gemm_f16
     _call(fn, dev, stream, ta, tb, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc)
+    return out
+
+
+def gemm_splitk(a, b, splits=0, out=None, workspace=None, stream=None):
+    """C = a @ b as gemm(), with K split over several workgroups per output
+    tile (gemm_bf16_splitk / gemm_f16_splitk).  splits: 0 lets the library
+    choose, 1 disables, 2-16 forces.  workspace: a 16-byte aligned CUDA
+    tensor of at least tgemm_splitk_workspace_bytes(M, N, splits) bytes;
+    allocated (uint8) when None."""
+    torch = _torch()
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not multiply")
+    if a.dtype != b.dtype or a.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("a and b must both be bfloat16 or both float16")
+    if a.device.type != "cuda" or b.device.type != "cuda":
+        raise ValueError("a and b must be on a GPU")
+    M, K = a.shape
+    N = b.shape[1]
+    ta, lda = _layout(a, "a")
+    tb, ldb = _layout(b, "b")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if out.dtype != a.dtype or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1):
+        raise ValueError("out must be a row-major (M, N) tensor of the input dtype")
+    ldc = max(out.stride(0), N)
+    need = lib().tgemm_splitk_workspace_bytes(M, N, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dev = _same_device(a=a, b=b, out=out, workspace=workspace)
+    fn = lib().gemm_bf16_splitk if a.dtype == torch.bfloat16 else lib().gemm_f16_splitk
+    _call(fn, dev, stream, ta, tb, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, splits,
+          workspace.data_ptr(), ws_bytes)
     return out
 
 

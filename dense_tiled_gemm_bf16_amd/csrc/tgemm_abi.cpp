@@ -134,7 +134,8 @@ int dispatch(const char *fn, tgemm::Problem p) {
 // C = op(A) op(B) for 16-bit inputs with any operand storage and row
 // strides (gemm_bf16 / gemm_f16).
 int gemm_general(const char *fn, tgemm::Dt dt, int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
-                 const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
+                 const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, int splits, void *ws,
+                 uint64_t ws_bytes, hipStream_t stream) {
   g_err[0] = '\0';
   if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
     return fail(TGEMM_EINVAL, "%s: trans_a and trans_b must be 0 or 1 (got %d, %d)", fn, trans_a, trans_b);
@@ -185,8 +186,26 @@ int gemm_general(const char *fn, tgemm::Dt dt, int trans_a, int trans_b, int64_t
   const uint64_t b_span = trans_b ? (uint64_t)tgemm::kTileN * ldb * 2 : k_rows_bytes(K, ldb);
   if (a_span > kOffsetLimit) return fail(TGEMM_ETOOBIG, "%s: A too large for 31-bit offsets", fn);
   if (b_span > kOffsetLimit) return fail(TGEMM_ETOOBIG, "%s: B too large for 31-bit offsets", fn);
+  if (splits < 0 || splits > tgemm::kMaxSplits)
+    return fail(TGEMM_EINVAL, "%s: splits=%d must be 0 (automatic) or 1 .. %d", fn, splits, tgemm::kMaxSplits);
+  if (splits != 1) {
+    // The workspace: fp32 partial sums, one M x N plane per split.
+    const uint64_t plane = (uint64_t)M * (uint64_t)N * 4u;
+    if (!ws && ws_bytes > 0) return fail(TGEMM_EINVAL, "%s: workspace is NULL", fn);
+    if (ws && misaligned(ws)) return fail(TGEMM_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+    if (splits >= 2 && ws_bytes < (uint64_t)splits * plane)
+      return fail(TGEMM_EINVAL, "%s: %d splits of a %lld x %lld output need %llu workspace bytes, got %llu", fn,
+                  splits, (long long)M, (long long)N, (unsigned long long)((uint64_t)splits * plane),
+                  (unsigned long long)ws_bytes);
+    // The part of the workspace a call may write: what its splits need.
+    const uint64_t most = (uint64_t)(splits == 0 ? tgemm::kAutoMaxSplits : splits) * plane;
+    const uint64_t used = ws_bytes < most ? ws_bytes : most;
+    for (const Operand &o : ops)
+      if (overlaps(ws, used, o.ptr, o.bytes)) return fail(TGEMM_EINVAL, "%s: workspace overlaps %s", fn, o.name);
+    if (overlaps(ws, used, C, c_bytes)) return fail(TGEMM_EINVAL, "%s: workspace overlaps C", fn);
+  }
   tgemm::Problem p{dt, trans_a == 1, trans_b == 1, M, N, K, A, lda, B, ldb, nullptr, nullptr, C, ldc, stream,
-                   0, 0, 0};
+                   0, 0, 0, splits, splits == 1 ? nullptr : ws, splits == 1 ? 0 : ws_bytes};
   return dispatch(fn, p);
 }
 
@@ -218,7 +237,7 @@ int gemm_mxfp4_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
   if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
   tgemm::Problem p{tgemm::Dt::kMxfp4, false, true, M, N, K, A, K / 2, B, K / 2, scale_A, scale_B, C, N, stream,
-                   0, 0, 0};
+                   0, 0, 0, 1, nullptr, 0};
   return dispatch(fn, p);
 }
 
@@ -241,18 +260,40 @@ int gemm_mxfp6_nt(int fmt, int64_t M, int64_t N, int64_t K, const void *A, const
   if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
   const tgemm::Dt dt = fmt == TGEMM_FP6_E2M3 ? tgemm::Dt::kMxfp6E2M3 : tgemm::Dt::kMxfp6E3M2;
-  tgemm::Problem p{dt, false, true, M, N, K, A, K / 4 * 3, B, K / 4 * 3, scale_A, scale_B, C, N, stream, 0, 0, 0};
+  tgemm::Problem p{dt, false, true, M, N, K, A, K / 4 * 3, B, K / 4 * 3, scale_A, scale_B, C, N, stream, 0, 0, 0, 1, nullptr, 0};
   return dispatch(fn, p);
 }
 
 int gemm_bf16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
               const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
-  return gemm_general("gemm_bf16", tgemm::Dt::kBf16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return gemm_general("gemm_bf16", tgemm::Dt::kBf16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, 1, nullptr,
+                      0, stream);
 }
 
 int gemm_f16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
              const void *B, int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
-  return gemm_general("gemm_f16", tgemm::Dt::kF16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return gemm_general("gemm_f16", tgemm::Dt::kF16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, 1, nullptr, 0,
+                      stream);
+}
+
+int gemm_bf16_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                     const void *B, int64_t ldb, void *C, int64_t ldc, int splits, void *workspace,
+                     uint64_t workspace_bytes, hipStream_t stream) {
+  return gemm_general("gemm_bf16_splitk", tgemm::Dt::kBf16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc,
+                      splits, workspace, workspace_bytes, stream);
+}
+
+int gemm_f16_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                    const void *B, int64_t ldb, void *C, int64_t ldc, int splits, void *workspace,
+                    uint64_t workspace_bytes, hipStream_t stream) {
+  return gemm_general("gemm_f16_splitk", tgemm::Dt::kF16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, splits,
+                      workspace, workspace_bytes, stream);
+}
+
+uint64_t tgemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {
+  if (M <= 0 || N <= 0 || splits < 0 || splits > tgemm::kMaxSplits) return 0;
+  const int s = splits == 0 ? tgemm::kAutoMaxSplits : splits == 1 ? 0 : splits;
+  return (uint64_t)s * (uint64_t)M * (uint64_t)N * 4u;
 }
 
 int quantize_mxfp8(int64_t M, int64_t K, const float *x, void *q, void *scales, hipStream_t stream) {
@@ -294,8 +335,7 @@ int tgemm_clock_probe(void *out, int *wallclock_khz, hipStream_t stream) {
   if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: wall-clock rate: %s", fn, hipGetErrorString(e));
   if (khz <= 0) return fail(TGEMM_EHIP, "%s: the device reports no constant-rate counter", fn);
   if (wallclock_khz) *wallclock_khz = khz;
-  // A spin of 10 us of constant-rate ticks.
-  e = tgemm::launch_clock_probe(out, (uint32_t)(khz / 100 > 0 ? khz / 100 : 1), stream);
+  e = tgemm::launch_clock_probe(out, stream);
   if (e != hipSuccess) return fail(TGEMM_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
   return TGEMM_OK;
 }
@@ -320,7 +360,7 @@ int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B, 
   if (rc != TGEMM_OK || M == 0 || N == 0) return rc;
   if ((uint64_t)tgemm::kTileM * k * 2 > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
-  tgemm::Problem p{tgemm::Dt::kBf16, false, true, M, N, K, A, K, B, K, nullptr, nullptr, C, N, stream, 0, 0, 0};
+  tgemm::Problem p{tgemm::Dt::kBf16, false, true, M, N, K, A, K, B, K, nullptr, nullptr, C, N, stream, 0, 0, 0, 1, nullptr, 0};
   return dispatch(fn, p);
 }
 
@@ -335,7 +375,7 @@ int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, v
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K * 2 bytes must stay below 2^31)", fn, (long long)K);
   if (k_rows_bytes(K, N) > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: B too large (K * N * 2 bytes, K rounded up to 64, must stay below 2^31)", fn);
-  tgemm::Problem p{tgemm::Dt::kF16, false, false, M, N, K, A, K, B, N, nullptr, nullptr, C, N, stream, 0, 0, 0};
+  tgemm::Problem p{tgemm::Dt::kF16, false, false, M, N, K, A, K, B, N, nullptr, nullptr, C, N, stream, 0, 0, 0, 1, nullptr, 0};
   return dispatch(fn, p);
 }
 
@@ -355,7 +395,7 @@ int gemm_mxfp8_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
     return fail(TGEMM_ETOOBIG, "%s: K=%lld too large (256 * K bytes must stay below 2^31)", fn, (long long)K);
   if (m * kb > kOffsetLimit || n * kb > kOffsetLimit)
     return fail(TGEMM_ETOOBIG, "%s: scale arrays too large", fn);
-  tgemm::Problem p{tgemm::Dt::kMxfp8, false, true, M, N, K, A, K, B, K, scale_A, scale_B, C, N, stream, 0, 0, 0};
+  tgemm::Problem p{tgemm::Dt::kMxfp8, false, true, M, N, K, A, K, B, K, scale_A, scale_B, C, N, stream, 0, 0, 0, 1, nullptr, 0};
   return dispatch(fn, p);
 }
 

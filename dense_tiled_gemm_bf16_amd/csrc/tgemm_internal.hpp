@@ -27,7 +27,18 @@ struct Problem {
   hipStream_t stream;
   int cus;             // compute units of the device
   int tile_m, tile_n;  // forced output tile, or 0, 0 to choose by shape
+  // K split (16-bit kinds): 1 = none; 0 = the library chooses (at most what
+  // ws_bytes holds); >= 2 = that many (at most one per 64-element K slice).
+  // ws: fp32 workspace of ws_bytes bytes (16-byte aligned) for the partial
+  // sums, splits planes of M x N.
+  int splits;
+  void *ws;
+  uint64_t ws_bytes;
 };
+
+// Most K splits of one call, and of an automatic choice.
+constexpr int kMaxSplits = 16;
+constexpr int kAutoMaxSplits = 4;
 
 // Largest output tile of one workgroup (rows of C x columns of C).
 constexpr int kTileM = 256;
@@ -53,13 +64,12 @@ struct QuantProblem {
 // Enqueues the quantiser for `p` on p.stream.  Returns the launch status.
 hipError_t launch_quantize(const QuantProblem &p);
 
-// Workgroups of the clock probe: one per XCD (8 on MI355X), in turn.
-constexpr int kProbeGroups = 8;
+// Workgroups of the clock probe: one per CU of an MI355X (8 XCDs x 32).
+constexpr int kProbeGroups = 256;
 
 // Enqueues the clock probe on `stream`: writes kProbeGroups records of four
-// uint64 {XCC id, s_memtime, s_memrealtime, spin} to the device buffer `out`,
-// spin = (constant-rate ticks << 32) | shader-clock ticks over a spin of
-// `ticks` constant-rate ticks.
-hipError_t launch_clock_probe(void *out, uint32_t ticks, hipStream_t stream);
+// uint64 {XCC id << 32 | HW_ID, s_memtime, s_memrealtime, 0} to the device
+// buffer `out`.
+hipError_t launch_clock_probe(void *out, hipStream_t stream);
 
 }  // namespace tgemm

@@ -53,6 +53,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -91,6 +92,11 @@ struct Args {
   int tiles_m, tiles_n;
   int ksteps;  // ceil(K / elements per slice)
   int kb;      // scale blocks per row (mxfp8)
+  // K split (16-bit kinds): workgroup w computes the tile w % tiles over
+  // slices [kq s, kq s + kq) with s = w / tiles, and writes its fp32 sums to
+  // plane s of ws (splits planes of M x N, rows N apart).
+  float *ws;
+  int splits, kq;
 };
 
 // Element type of A and B, and the storage of each: AK, A is M x K
@@ -350,8 +356,9 @@ struct Slots {
   LDS_AS uint8_t *junk;  // 256 bytes per wave: landing area of the L2 prefetches
 };
 
-template <class T, int TM, int TN>
+template <class T, int TM, int TN, bool SPLIT = false>
 struct Kernel {
+  static_assert(!SPLIT || !T::kScaled, "the K split is for the 16-bit kinds");
   static constexpr int kNS = kSlots<T, TM, TN>;
   static constexpr int kElem = T::kElem;
   static constexpr int kWM = TM / 2, kWN = TN / 2;   // wave tile (2 x 2 waves)
@@ -452,6 +459,7 @@ struct Kernel {
   int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
+  int kK;  // K of this workgroup's range (all of K unless split)
   int zt;  // the ragged last slice (or the only, all-zero one when K = 0); -1 if none
   typename std::conditional<T::kFp6, DenseLoader<kLA>,
                             typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type>::type la;
@@ -703,18 +711,18 @@ struct Kernel {
   __device__ __forceinline__ void load_one(int kt, int i) {
     if (i < kLA) {
       if constexpr (T::kFp6)
-        la.issue(slots.a[S], wave, kt, a.K, kSliceK, i);
+        la.issue(slots.a[S], wave, kt, kK, kSliceK, i);
       else if constexpr (T::kScaled && !T::kWholeK)
-        la.issue_masked(slots.a[S], wave, kt, a.K, kSliceK, i);
+        la.issue_masked(slots.a[S], wave, kt, kK, kSliceK, i);
       else if constexpr (T::kAK)
         la.issue(slots.a[S], wave, kt, i);
       else
         la.issue(slots.a[S], wave, kt, nk, i);
     } else {
       if constexpr (T::kFp6)
-        lb.issue(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
+        lb.issue(slots.b[S], wave, kt, kK, kSliceK, i - kLA);
       else if constexpr (T::kScaled && !T::kWholeK)
-        lb.issue_masked(slots.b[S], wave, kt, a.K, kSliceK, i - kLA);
+        lb.issue_masked(slots.b[S], wave, kt, kK, kSliceK, i - kLA);
       else if constexpr (T::kBK)
         lb.issue(slots.b[S], wave, kt, i - kLA);
       else
@@ -729,15 +737,15 @@ struct Kernel {
   static constexpr bool kZeroTail = !T::kScaled && (T::kAK || T::kBK);
   template <int S>
   __device__ __forceinline__ void zero_tail(int kt) {
-    if constexpr (T::kAK && !T::kFp6) la.zero_tail(slots.a[S], wave, lane, kt, a.K, kSliceK);
-    if constexpr (T::kBK && !T::kFp6) lb.zero_tail(slots.b[S], wave, lane, kt, a.K, kSliceK);
+    if constexpr (T::kAK && !T::kFp6) la.zero_tail(slots.a[S], wave, lane, kt, kK, kSliceK);
+    if constexpr (T::kBK && !T::kFp6) lb.zero_tail(slots.b[S], wave, lane, kt, kK, kSliceK);
     wait_vm_lgkm0<63>();
   }
 
   // One dword of each 128-byte line of slice kt of this workgroup's share of
   // the A and B panels; out-of-range rows and slices past K load nothing.
   __device__ __forceinline__ void prefetch(int kt) {
-    const bool ok = kt * kSliceK < a.K;
+    const bool ok = kt * kSliceK < kK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (LDS_AS void *)(slots.junk + wave * 256), 4,
                                              ok ? pf_off : kOOB, (uint32_t)kt * T::kSliceBytes, 0, 0);
   }
@@ -924,25 +932,39 @@ struct Kernel {
     lane_sw = swz(lane & 15);  // fragment blocks start at multiples of 16 rows
 
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int wg = (int)blockIdx.x;
+    const int split = SPLIT ? wg / tiles : 0;
+    tile_of(SPLIT ? wg - split * tiles : wg, tiles, a.tiles_m, a.tiles_n, tm, tn);
     m0 = tm * TM;
     n0 = tn * TN;
-    const int K = a.K;
+    // This workgroup's K range: all of K, or (split) slices [kq s, kq s + kq)
+    // clipped to K, i.e. the K elements from k0 on.  The loaders are based at
+    // column (K-contiguous) or row (K-major) k0 and see a K of kK.
+    int k0 = 0;
+    kK = a.K;
     nk = a.ksteps;
-    zt = a.K % kSliceK != 0 || nk == 0 ? (nk > 0 ? nk - 1 : 0) : -1;
+    if constexpr (SPLIT) {
+      const int s0 = split * a.kq;
+      nk = min(a.kq, a.ksteps - s0);
+      k0 = s0 * kSliceK;
+      kK = min(a.K - k0, nk * kSliceK);
+    }
+    const int K = kK;
+    zt = K % kSliceK != 0 || nk == 0 ? (nk > 0 ? nk - 1 : 0) : -1;
 
     if constexpr (T::kFp6)
       la.init(a.A + (size_t)m0 * a.lda, min(a.M - m0, TM), K, a.lda, wave, lane);
     else if constexpr (T::kAK)
-      la.init(a.A + (size_t)m0 * a.lda * kElem, min(a.M - m0, TM), K, a.lda, kElem, kSliceK, wave, lane);
+      la.init(a.A + ((size_t)m0 * a.lda + k0) * kElem, min(a.M - m0, TM), K, a.lda, kElem, kSliceK, wave, lane);
     else
-      la.init(a.A, K, a.M, m0, a.lda, wave, lane);
+      la.init(a.A + (size_t)k0 * a.lda * kElem, K, a.M, m0, a.lda, wave, lane);
     if constexpr (T::kFp6)
       lb.init(a.B + (size_t)n0 * a.ldb, min(a.N - n0, TN), K, a.ldb, wave, lane);
     else if constexpr (T::kBK)
-      lb.init(a.B + (size_t)n0 * a.ldb * kElem, min(a.N - n0, TN), K, a.ldb, kElem, kSliceK, wave, lane);
+      lb.init(a.B + ((size_t)n0 * a.ldb + k0) * kElem, min(a.N - n0, TN), K, a.ldb, kElem, kSliceK, wave, lane);
     else
-      lb.init(a.B, K, a.N, n0, a.ldb, wave, lane);
+      lb.init(a.B + (size_t)k0 * a.ldb * kElem, K, a.N, n0, a.ldb, wave, lane);
     if constexpr (T::kFp6) {
       // Fragment rows start at multiples of 32, so a lane's row has rot6 of
       // lane % 32.  Logical 8-byte piece 6 s + 3 (l / 32) + q of the row.
@@ -1071,7 +1093,29 @@ struct Kernel {
     // can finish.
     wait_vm_lgkm0<0>();
     fence_acc();
-    epilogue();
+    if constexpr (SPLIT)
+      epilogue_partial(split);
+    else
+      epilogue();
+  }
+
+  // K split: the tile's fp32 sums into plane `split` of the workspace (M x N,
+  // rows N apart).  16 x 16 blocks: lane l holds row l % 16, columns
+  // 4 (l / 16) .. + 3, one 16-byte store each (N % 8 == 0, so a group of four
+  // columns is all in or all out of range).
+  __device__ __forceinline__ void epilogue_partial(int split) {
+    static_assert(kBlk == 16, "16 x 16 blocks");
+    float *plane = a.ws + (size_t)split * (size_t)a.M * (size_t)a.N;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < kNBm; ++j) {
+      const int m = m0 + wave_m * kWM + j * kBlk + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < kNBn; ++i) {
+        const int n = n0 + wave_n * kWN + i * kBlk + 4 * q;
+        if (m < a.M && n < a.N) *(f32x4 *)(plane + (size_t)m * a.N + n) = acc[i][j];
+      }
+    }
   }
 
   // acc[i][j] covers B rows (C columns) n0 + kWN wave_n + kBlk i and A rows
@@ -1177,7 +1221,7 @@ struct Kernel {
 
 // One workgroup per CU: either shape's ring takes 128 KiB of the 160 KiB
 // LDS, and a 256-row tile's accumulators fill a SIMD's registers.
-template <class T, int TM, int TN>
+template <class T, int TM, int TN, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body is device code only; the host pass needs the symbol
@@ -1211,23 +1255,94 @@ void gemm_kernel(const Args a) {
     slots.b[3] = (LDS_AS uint8_t *)sB3;
   }
   slots.junk = (LDS_AS uint8_t *)junk;
-  Kernel<T, TM, TN> k(a, slots);
+  Kernel<T, TM, TN, SPLIT> k(a, slots);
   k.run();
 #endif
 }
 
-template <class T, int TM, int TN>
+template <class T, int TM, int TN, bool SPLIT = false>
 hipError_t launch_shape(const Problem &p, Args a) {
   a.tiles_m = (int)((p.M + TM - 1) / TM);
   a.tiles_n = (int)((p.N + TN - 1) / TN);
   // A dispatch holds fewer than 2^32 work-items per dimension.
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-  if (tiles > (int64_t)(UINT32_MAX / kThreads)) return hipErrorInvalidConfiguration;
+  const int64_t wgs = tiles * (SPLIT ? a.splits : 1);
+  if (wgs > (int64_t)(UINT32_MAX / kThreads)) return hipErrorInvalidConfiguration;
   // hipLaunchKernel returns this launch's own status (hipGetLastError could
   // report an earlier, unrelated failure of the calling thread).
   void *args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, TM, TN>), dim3((unsigned)tiles),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<T, TM, TN, SPLIT>), dim3((unsigned)wgs),
                          dim3(kThreads), args, 0, p.stream);
+}
+
+// K split, second pass: C[m][n] = the sum over s = 0, 1, ... splits - 1, in
+// that order, of plane s [m][n], rounded to nearest-even bf16 (DT = kBf16)
+// or fp16.  One thread per 8 consecutive columns of a row (N % 8 == 0):
+// two 16-byte loads per plane, one 16-byte store.
+struct ReduceArgs {
+  const float *ws;
+  uint8_t *C;
+  int splits, M, N, ldc;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs r) {
+  const int per_row = r.N >> 3;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)r.M * per_row) return;
+  const int m = (int)(g / per_row);
+  const int n = (int)(g - (int64_t)m * per_row) * 8;
+  const size_t plane = (size_t)r.M * (size_t)r.N;
+  const float *p = r.ws + (size_t)m * r.N + n;
+  f32x4 lo = *(const f32x4 *)p, hi = *(const f32x4 *)(p + 4);
+  for (int s = 1; s < r.splits; ++s) {
+    lo += *(const f32x4 *)(p + s * plane);
+    hi += *(const f32x4 *)(p + s * plane + 4);
+  }
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 &v = h ? hi : lo;
+    const f32x2 x = {v[0], v[1]}, y = {v[2], v[3]};
+    if constexpr (DT == kF16) {
+      out[2 * h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+      out[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, f16x2));
+    } else {
+      out[2 * h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+      out[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+    }
+  }
+  *(u32x4 *)(r.C + ((size_t)m * r.ldc + n) * 2) = out;
+}
+
+template <int DT>
+hipError_t launch_reduce(const Problem &p, const Args &a) {
+  ReduceArgs r{a.ws, a.C, a.splits, a.M, a.N, a.ldc};
+  const int64_t blocks = ((int64_t)p.M * (p.N / 8) + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  void *args[] = {&r};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel<DT>), dim3((unsigned)blocks),
+                         dim3(256), args, 0, p.stream);
+}
+
+// The K-split pair of one layout: partial sums, then the reduction.
+template <int DT, bool AK, bool BK>
+hipError_t launch_split_layout(const Problem &p, const Args &a, int tm, int tn) {
+  using T = Traits<DT, AK, BK>;
+  hipError_t e = hipErrorInvalidValue;
+  if (tm == 128 && tn == 128) e = launch_shape<T, 128, 128, true>(p, a);
+  else if (tm == 64 && tn == 64) e = launch_shape<T, 64, 64, true>(p, a);
+  if (e != hipSuccess) return e;
+  return launch_reduce<DT>(p, a);
+}
+
+template <int DT>
+hipError_t launch_split_dt(const Problem &p, const Args &a, int tm, int tn) {
+  const bool ak = !p.trans_a, bk = p.trans_b;
+  if (ak && bk) return launch_split_layout<DT, true, true>(p, a, tm, tn);
+  if (ak) return launch_split_layout<DT, true, false>(p, a, tm, tn);
+  if (bk) return launch_split_layout<DT, false, true>(p, a, tm, tn);
+  return launch_split_layout<DT, false, false>(p, a, tm, tn);
 }
 
 // The 16-bit kernels of one operand layout, by tile shape (256 x 192 only
@@ -1297,6 +1412,45 @@ Shape pick_shape(const Shape (&shapes)[NS], int64_t M, int64_t N, int cus) {
   return best;
 }
 
+// Whether to split K, and into how many pieces of which tile shape.  Only
+// the 128 x 128 and 64 x 64 tiles have split kernels; with another tile
+// forced there is no split (the front end refuses explicit splits then).
+// Explicit splits are taken as given (the caller's workspace holds them).
+// Automatic ones (p.splits == 0) only where the plain grid leaves at least
+// half the CUs idle and K has at least 48 slices (3072 elements): then
+// 64 x 64 tiles and at most 4 splits, no more than fill the CUs once, at
+// least 16 slices each, and no more than the workspace holds.  Measured
+// under graph replay (bf16 NT, us per call, plain -> split): 512 x 512 x 4096
+// 10.95 -> 9.68 (3 splits 9.3, 6 splits 12.7), 512 x 512 x 8192 22.5 -> 13.1,
+// 256 x 256 x 4096 10.8 -> 7.7; but 768 x 512 x 2048 (32 slices) 6.7 -> 8.4
+// with 2 splits: the partial sums' round trip and the second kernel cost
+// about 2-3 us, which short K ranges do not repay.  Returns false for no
+// split (tm, tn untouched).
+bool choose_split(const Problem &p, int ksteps, int &tm, int &tn, int &splits) {
+  const bool forced = p.tile_m != 0;
+  if (forced && !((p.tile_m == 128 && p.tile_n == 128) || (p.tile_m == 64 && p.tile_n == 64))) return false;
+  const uint64_t plane = (uint64_t)p.M * (uint64_t)p.N * 4u;
+  const int64_t fit = plane > 0 ? (int64_t)(p.ws_bytes / plane) : 0;
+  if (p.splits >= 2) {
+    splits = (int)std::min<int64_t>({(int64_t)p.splits, (int64_t)kMaxSplits, (int64_t)ksteps, fit});
+    if (splits < 2) return false;
+    tm = forced ? p.tile_m : 64;
+    tn = forced ? p.tile_n : 64;
+    return true;
+  }
+  const Shape plain = p.trans_b ? pick_shape(kShapesBK, p.M, p.N, p.cus) : pick_shape(kShapesBN, p.M, p.N, p.cus);
+  const int64_t plain_tiles = ((p.M + plain.tm - 1) / plain.tm) * ((p.N + plain.tn - 1) / plain.tn);
+  if (plain_tiles * 2 > p.cus || ksteps < 48) return false;
+  const int stm = forced ? p.tile_m : 64, stn = forced ? p.tile_n : 64;
+  const int64_t tiles = ((p.M + stm - 1) / stm) * ((p.N + stn - 1) / stn);
+  const int64_t want = std::min<int64_t>({(int64_t)p.cus / tiles, (int64_t)kAutoMaxSplits, (int64_t)ksteps / 16, fit});
+  if (want < 2) return false;
+  splits = (int)want;
+  tm = stm;
+  tn = stn;
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch(const Problem &p) {
@@ -1312,6 +1466,9 @@ hipError_t launch(const Problem &p) {
   a.lda = (int)p.lda;
   a.ldb = (int)p.ldb;
   a.ldc = (int)p.ldc;
+  a.ws = nullptr;
+  a.splits = 1;
+  a.kq = 0;
   const int slice = p.dt == Dt::kMxfp8 ? 128 : 64;
   a.ksteps = (int)((p.K + slice - 1) / slice);
   a.kb = (int)((p.K + 127) / 128);
@@ -1333,6 +1490,16 @@ hipError_t launch(const Problem &p) {
   // loads check no columns (2% fewer cycles).
   const bool whole = p.K > 0 && p.K % 128 == 0;
   int tm = p.tile_m, tn = p.tile_n;
+  if ((p.dt == Dt::kBf16 || p.dt == Dt::kF16) && p.splits != 1 && p.ws != nullptr) {
+    int splits = 0;
+    if (choose_split(p, a.ksteps, tm, tn, splits)) {
+      // Whole slices per split, and no split left empty.
+      a.kq = (a.ksteps + splits - 1) / splits;
+      a.splits = (a.ksteps + a.kq - 1) / a.kq;
+      a.ws = static_cast<float *>(p.ws);
+      return p.dt == Dt::kBf16 ? launch_split_dt<kBf16>(p, a, tm, tn) : launch_split_dt<kF16>(p, a, tm, tn);
+    }
+  }
   if (tm == 0) {
     const Shape s = scaled             ? Shape{256, 256, 1.0}
                     : p.trans_b        ? pick_shape(kShapesBK, p.M, p.N, p.cus)
@@ -1369,6 +1536,7 @@ hipError_t launch(const Problem &p) {
 
 bool shape_supported(const Problem &p, int tile_m, int tile_n) {
   if (p.dt != Dt::kBf16 && p.dt != Dt::kF16) return tile_m == 256 && tile_n == 256;
+  if (p.splits >= 2) return (tile_m == 128 && tile_n == 128) || (tile_m == 64 && tile_n == 64);
   return (tile_m == 256 && tile_n == 256) || (tile_m == 128 && tile_n == 128) || (tile_m == 64 && tile_n == 64) ||
          (tile_m == 256 && tile_n == 192 && p.trans_b);
 }

@@ -217,6 +217,59 @@ TGEMM_API int gemm_f16(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
                        void *C, int64_t ldc, hipStream_t stream);
 
 /*
+ * C = op(A) . op(B) as gemm_bf16 / gemm_f16, with the K range split over
+ * several workgroups per output tile, for problems with too few output tiles
+ * to fill the GPU's compute units (M x N small, K deep).
+ *
+ * The pages give each output tile one thread block for all of K (TileLang
+ * SM100 README, "Code Example": T.Kernel over ceil-div tiles of N and M,
+ * T.Pipelined over all of K) and point to a persistent, warp-specialised
+ * GEMM for scheduling work onto the machine (Blackwell TCGEN05 GEMM
+ * tutorial, section "进阶" (Advanced)).  Here, when the tiles are fewer than
+ * the CUs, each tile's K slices are divided into `splits` contiguous ranges
+ * computed by different workgroups: each writes its fp32 sums to one plane
+ * of the workspace, and a second kernel on the same stream adds the planes
+ * in order (plane 0 first) and rounds once to the output type.  No device-
+ * scope synchronisation is used: the kernel boundary orders the two passes.
+ *
+ * Arguments and requirements as for gemm_bf16 / gemm_f16, plus:
+ *   splits           0: the library chooses (no split unless the plain grid
+ *                    leaves at least half the CUs idle and K >= 3072; then
+ *                    64 x 64 tiles and at most 4 splits of at least 1024 K
+ *                    elements each, no more than the workspace holds);
+ *                    1: no split (the workspace is not used); 2 .. 16: that
+ *                    many (at most one per 64 K elements: more are clipped)
+ *   workspace        device pointer, 16-byte aligned, owned by the caller,
+ *                    not overlapping A, B or C; may be NULL when splits == 1
+ *   workspace_bytes  its size; at least splits * M * N * 4 for splits >= 2
+ *                    (tgemm_splitk_workspace_bytes); its contents on entry
+ *                    do not matter and are left undefined
+ * Sums are fp32; the order differs from gemm_bf16's only in that the split
+ * ranges' sums are added at the end, in range order, so the result is
+ * deterministic.  A forced tile (tgemm_set_tile) must be 128 x 128 or
+ * 64 x 64 for splits >= 2 (TGEMM_EINVAL otherwise); other forced tiles run
+ * without a split when splits == 0.  Returns TGEMM_EINVAL for splits outside
+ * 0 .. 16, a NULL or too small workspace, or a workspace overlapping an
+ * operand, TGEMM_EALIGN for a misaligned workspace.
+ */
+TGEMM_API int gemm_bf16_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                               const void *A, int64_t lda, const void *B, int64_t ldb,
+                               void *C, int64_t ldc, int splits, void *workspace,
+                               uint64_t workspace_bytes, hipStream_t stream);
+TGEMM_API int gemm_f16_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                              const void *A, int64_t lda, const void *B, int64_t ldb,
+                              void *C, int64_t ldc, int splits, void *workspace,
+                              uint64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes gemm_bf16_splitk / gemm_f16_splitk use for an M x N output
+ * with `splits` splits: splits * M * N * 4; for splits == 0 the most the
+ * automatic choice can use (4 * M * N * 4); 0 for splits == 1 or invalid
+ * arguments.
+ */
+TGEMM_API uint64_t tgemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
+
+/*
  * Block-scale quantiser: binary32 rows to the operand format of
  * gemm_mxfp8_nt (the step before the block-scaled GEMM; one scale per 128 K
  * elements as in the Blackwell TCGEN05 GEMM tutorial, section "进阶"
@@ -262,20 +315,20 @@ TGEMM_API const char *tgemm_last_error(void);
  * Shader-clock probe, a measurement helper off the GEMM path.  The pages
  * time a kernel and report TFLOPS = 2 M N K / t (TileLang SM100 README,
  * "Compilation and Usage"); on MI355X that time also depends on the shader
- * clock the board's power limit allows.  Each of the probe's workgroups
- * reads its XCD's shader-clock counter (s_memtime) and constant-rate counter
- * (s_memrealtime), spins for 10 us of constant-rate ticks and reads both
- * again; the ratio of the two differences times the constant rate is that
- * XCD's clock at that moment.  Enqueued right after a timed region, it gives
- * the clock the region ended at.
+ * clock the board's power limit allows.  The probe runs one single-wave
+ * workgroup per CU (256), each reading its CU's shader-clock counter
+ * (s_memtime) and the constant-rate counter (s_memrealtime).  Every CU has
+ * a shader-clock counter of its own, so two probes give a CU's average
+ * clock between them from records of the same CU only:
+ * (difference of the shader-clock counts) / (difference of the constant-rate
+ * counts) * the constant rate.
  *
- *   out            device pointer to 32 uint64 (256 bytes), 16-byte
- *                  aligned, owned by the caller; written on `stream` with 8
- *                  records, one per workgroup (the workgroups go to the XCDs
- *                  in turn): {XCC id, shader-clock count and constant-rate
- *                  count at the start of the spin, spin}, where spin holds
- *                  the constant-rate ticks of the spin in its upper 32 bits
- *                  and the shader-clock ticks in its lower 32 bits
+ *   out            device pointer to 1024 uint64 (8 KiB), 16-byte aligned,
+ *                  owned by the caller; written on `stream` with 256
+ *                  records of four uint64, one per workgroup:
+ *                  {XCC id << 32 | HW_ID (bits 8-11 CU, bit 12 shader
+ *                  array, bits 13-15 shader engine), shader-clock count,
+ *                  constant-rate count, 0}
  *   wallclock_khz  host pointer, may be NULL; receives the constant-rate
  *                  counter's frequency in kHz (written before returning)
  *

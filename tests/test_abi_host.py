@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
         ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_mxfp4_nt", "gemm_mxfp6_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
-         "tgemm_last_error", "tgemm_set_tile", "tgemm_clock_probe"])
+         "tgemm_last_error", "tgemm_set_tile", "tgemm_clock_probe", "gemm_bf16_splitk", "gemm_f16_splitk",
+         "tgemm_splitk_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -257,3 +258,24 @@ def test_clock_probe_validation():
     assert "out is NULL" in tg.last_error()
     assert L.tgemm_clock_probe(A16 + 8, ctypes.byref(khz), None) == tg.EALIGN
     assert "aligned" in tg.last_error()
+
+
+def test_splitk_validation():
+    L = tg.lib()
+    M, N, K = 64, 64, 256
+    ws = 0x60000000
+    need = L.tgemm_splitk_workspace_bytes(M, N, 2)
+    assert need == 2 * M * N * 4
+    assert L.tgemm_splitk_workspace_bytes(M, N, 0) == 4 * M * N * 4
+    assert L.tgemm_splitk_workspace_bytes(M, N, 1) == 0
+    assert L.tgemm_splitk_workspace_bytes(M, N, 17) == 0
+    assert L.tgemm_splitk_workspace_bytes(0, N, 2) == 0
+    call = lambda splits, w, nb: L.gemm_bf16_splitk(0, 1, M, N, K, A16, K, B16, K, C16, N, splits, w, nb, None)
+    assert call(17, ws, need) == tg.EINVAL and "splits" in tg.last_error()
+    assert call(-1, ws, need) == tg.EINVAL
+    assert call(2, ws, need - 1) == tg.EINVAL and "workspace bytes" in tg.last_error()
+    assert call(2, None, need) == tg.EINVAL and "NULL" in tg.last_error()
+    assert call(2, ws + 8, need) == tg.EALIGN
+    assert call(2, A16, need) == tg.EINVAL and "overlaps A" in tg.last_error()
+    assert call(2, C16 - 16, need) == tg.EINVAL and "overlaps C" in tg.last_error()
+    assert L.gemm_f16_splitk(0, 0, M, N, K, A16, K, B16, N, C16, N, 3, ws, need, None) == tg.EINVAL

@@ -70,6 +70,9 @@ WORKLOADS = {
                  "bf16 NT GEMM M=4096 N=4096 K=8192"),
         Workload("bf16_nt_4000x3000x5000", "bf16_nt", 4000, 3000, 5000,
                  "bf16 NT GEMM M=4000 N=3000 K=5000 (ragged tails)"),
+        # Few output tiles, deep K: the case the K split is for.
+        Workload("bf16_nt_512x512x4096", "bf16_nt", 512, 512, 4096,
+                 "bf16 NT GEMM M=N=512 K=4096 (few tiles, deep K)"),
         Workload("mxfp8_nt_4096", "mxfp8_nt", 4096, 4096, 4096,
                  "block-scaled fp8 (e4m3 + e8m0 per 128 K) NT GEMM M=N=K=4096"),
         # The step before the block-scaled GEMM: one of its operands, quantised.
