@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64, ctypes.c_int, p,
                       ctypes.c_uint64, p]
         f.restype = ctypes.c_int
+    L.gemm_bf16_splitk_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64,
+                                           ctypes.c_int, p]
+    L.gemm_bf16_splitk_noalloc.restype = ctypes.c_int
     L.tgemm_splitk_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
     L.tgemm_splitk_workspace_bytes.restype = ctypes.c_uint64
     L.tgemm_clock_probe.argtypes = [p, ctypes.POINTER(ctypes.c_int), p]

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtgemm.so")
 SOURCES = [os.path.join(CSRC, "tgemm_kernels.hip"), os.path.join(CSRC, "tgemm_quant.hip"),
-           os.path.join(CSRC, "tgemm_clock.hip"), os.path.join(CSRC, "tgemm_abi.cpp")]
+           os.path.join(CSRC, "tgemm_clock.hip"), os.path.join(CSRC, "tgemm_scratch.hip"),
+           os.path.join(CSRC, "tgemm_abi.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

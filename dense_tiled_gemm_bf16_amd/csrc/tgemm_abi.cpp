@@ -54,6 +54,15 @@ void init_device(int dev) {
     return;
   }
   g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  // The no-allocation entry point's scratch: its device address on this
+  // device (the device is current here).
+  e = tgemm::scratch_init(dev);
+  if (e != hipSuccess) {
+    g_dev_status[dev] = TGEMM_EHIP;
+    snprintf(g_dev_msg[dev], sizeof g_dev_msg[dev], "device %d: address of the scratch array: %s", dev,
+             hipGetErrorString(e));
+    return;
+  }
   g_dev_status[dev] = TGEMM_OK;
 }
 
@@ -288,6 +297,30 @@ int gemm_f16_splitk(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, c
                     uint64_t workspace_bytes, hipStream_t stream) {
   return gemm_general("gemm_f16_splitk", tgemm::Dt::kF16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, splits,
                       workspace, workspace_bytes, stream);
+}
+
+int gemm_bf16_splitk_noalloc(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                             const void *B, int64_t ldb, void *C, int64_t ldc, int splits, hipStream_t stream) {
+  static const char fn[] = "gemm_bf16_splitk_noalloc";
+  g_err[0] = '\0';
+  if (splits >= 2 && M > 0 && N > 0 &&
+      (uint64_t)splits * (uint64_t)M * (uint64_t)N * 4u > tgemm::kScratchBytes)
+    return fail(TGEMM_ETOOBIG, "%s: %d splits of a %lld x %lld output need %llu bytes of scratch; it holds %llu", fn,
+                splits, (long long)M, (long long)N,
+                (unsigned long long)((uint64_t)splits * (uint64_t)M * (uint64_t)N * 4u),
+                (unsigned long long)tgemm::kScratchBytes);
+  int dev = -1;
+  void *ws = nullptr;
+  if (splits != 1 && M > 0 && N > 0) {
+    // Set up the device first (scratch_init runs there), then take its
+    // copy's address; never the array's host-side name.
+    int rc = ensure_device();
+    if (rc != TGEMM_OK) return rc;
+    if (hipGetDevice(&dev) != hipSuccess || !(ws = tgemm::scratch_ptr(dev)))
+      return fail(TGEMM_EHIP, "%s: no scratch address for the current device", fn);
+  }
+  return gemm_general(fn, tgemm::Dt::kBf16, trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, splits, ws,
+                      ws ? tgemm::kScratchBytes : 0, stream);
 }
 
 uint64_t tgemm_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {

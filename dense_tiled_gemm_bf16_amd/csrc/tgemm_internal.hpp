@@ -64,6 +64,18 @@ struct QuantProblem {
 // Enqueues the quantiser for `p` on p.stream.  Returns the launch status.
 hipError_t launch_quantize(const QuantProblem &p);
 
+// Device scratch of the no-allocation K split (tgemm_scratch.hip): bytes
+// per device, and the devices it is set up for.
+constexpr uint64_t kScratchBytes = 8ull << 20;
+constexpr int kMaxScratchDevices = 64;
+
+// With `dev` current: fetch the device address of dev's copy of the scratch
+// array (once per device; later calls return the first status).
+hipError_t scratch_init(int dev);
+
+// That address (nullptr until scratch_init(dev) has succeeded).
+void *scratch_ptr(int dev);
+
 // Workgroups of the clock probe: one per CU of an MI355X (8 XCDs x 32).
 constexpr int kProbeGroups = 256;
 

@@ -262,6 +262,27 @@ TGEMM_API int gemm_f16_splitk(int trans_a, int trans_b, int64_t M, int64_t N, in
                               uint64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gemm_bf16_splitk for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation and arguments, without the workspace:
+ * the partial sums go to a scratch array of 8 MiB that the library holds on
+ * each GPU it runs on until the process ends (set up with the device, no
+ * allocation per call).  This entry point calls no hipMalloc, hipFree or
+ * other allocating routine.
+ *
+ * Limits: splits * M * N * 4 <= 8 MiB for splits >= 2, else TGEMM_ETOOBIG;
+ * splits == 0 chooses within the scratch (no split when even two planes do
+ * not fit).  Every call on one GPU uses that GPU's one scratch array, so
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and may corrupt each other's results; calls on one stream run in
+ * order and are safe.  Nothing in the scratch needs clearing: every element
+ * a call reads it has written first.
+ */
+TGEMM_API int gemm_bf16_splitk_noalloc(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                                       const void *A, int64_t lda, const void *B, int64_t ldb,
+                                       void *C, int64_t ldc, int splits, hipStream_t stream);
+
+/*
  * Workspace bytes gemm_bf16_splitk / gemm_f16_splitk use for an M x N output
  * with `splits` splits: splits * M * N * 4; for splits == 0 the most the
  * automatic choice can use (4 * M * N * 4); 0 for splits == 1 or invalid

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
         ["gemm_bf16_nt", "gemm_f16_nn", "gemm_mxfp8_nt", "gemm_mxfp4_nt", "gemm_mxfp6_nt", "gemm_bf16", "gemm_f16", "quantize_mxfp8", "tgemm_init",
          "tgemm_last_error", "tgemm_set_tile", "tgemm_clock_probe", "gemm_bf16_splitk", "gemm_f16_splitk",
-         "tgemm_splitk_workspace_bytes"])
+         "tgemm_splitk_workspace_bytes", "gemm_bf16_splitk_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -279,3 +279,12 @@ def test_splitk_validation():
     assert call(2, A16, need) == tg.EINVAL and "overlaps A" in tg.last_error()
     assert call(2, C16 - 16, need) == tg.EINVAL and "overlaps C" in tg.last_error()
     assert L.gemm_f16_splitk(0, 0, M, N, K, A16, K, B16, N, C16, N, 3, ws, need, None) == tg.EINVAL
+
+
+def test_noalloc_splitk_rejects_what_the_scratch_cannot_hold():
+    L = tg.lib()
+    M, N, K = 1024, 1024, 4096      # 3 planes of 4 MiB > 8 MiB
+    rc = L.gemm_bf16_splitk_noalloc(0, 1, M, N, K, A16, K, B16, K, C16, N, 3, None)
+    assert rc == tg.ETOOBIG and "scratch" in tg.last_error()
+    assert L.gemm_bf16_splitk_noalloc(0, 1, M, N, K, A16, K, B16, K, C16, N, 17, None) in (tg.EINVAL, tg.ETOOBIG)
+    assert L.gemm_bf16_splitk_noalloc(0, 1, 0, N, K, A16, K, B16, K, C16, N, 2, None) == tg.OK
