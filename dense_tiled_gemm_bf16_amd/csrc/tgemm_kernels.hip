@@ -134,9 +134,21 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
 }
 
-// Wait states between inline-asm MFMAs and VALU code that touches their
-// registers, which the compiler's hazard tracking does not see: 24 idle
-// cycles cover the longest MFMA result latency of the forms used here.
+// Wait states between the last MFMAs and VALU code that reads their
+// accumulators.  The 16-bit MFMAs are inline asm, which the compiler's hazard
+// tracking does not see as MFMAs, so the required states are written out.
+// The CDNA3/CDNA4 rule for an XDL MFMA writing a register that a later VALU
+// instruction reads is a number of wait states that grows with the MFMA's
+// passes; for gfx950 the compiler's own hazard recognizer places, for the
+// builtins of the forms used here, 8 wait states after
+// v_mfma_f32_16x16x32_bf16/_f16 (4 passes), 12 after the scaled 32 x 32 x 64
+// form on fp4/fp6 (8 passes) and 20 after it on fp8 (16 passes) before a
+// dependent v_mul_f32 (checked on this build's own assembly).  Three
+// s_nop 7 give 24.  Between MFMAs no states are needed: consecutive MFMAs
+// write different accumulators, an accumulator is read again as SrcC only
+// by the same form 64 (16-bit) or 16 (scaled) MFMAs later, and the fragment
+// registers an MFMA reads (SrcA/B, read in its first pass) are rewritten
+// only by LDS reads issued after it, whose data returns tens of cycles later.
 __device__ __forceinline__ void mfma_fence() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
