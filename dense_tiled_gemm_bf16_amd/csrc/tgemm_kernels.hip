@@ -365,8 +365,10 @@ constexpr int kSlots = T::kFp6 ? 3 : (!T::kScaled && TM * TN <= 128 * 128) ? 4 :
 struct Slots {
   LDS_AS uint8_t *a[4];
   LDS_AS uint8_t *b[4];
-  LDS_AS uint8_t *junk;  // 256 bytes per wave: landing area of the L2 prefetches
+  LDS_AS uint8_t *junk;      // 256 bytes per wave: landing area of the L2 prefetches
+  LDS_AS uint8_t *stage[2];  // fp4, fp6: two buffers of one 16-byte scale chunk for each of the 512 rows
 };
+
 
 template <class T, int TM, int TN, bool SPLIT = false>
 struct Kernel {
@@ -503,7 +505,20 @@ struct Kernel {
   __amdgpu_buffer_rsrc_t rss[2];  // B scales, A scales; based at the tile's first row, dword aligned
   uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
-  u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction
+  u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction (fp6: chunk c only)
+  // fp4, fp6: a scale chunk of every row of the tile is loaded into LDS once
+  // per workgroup (waves 0-1 the B rows, waves 2-3 the A rows, 64 rows per
+  // load instruction) and each wave then reads the rows its MFMAs take (every
+  // row feeds two waves).  The per-lane loads from global memory touch one
+  // cache line per lane, so loading each row once instead of twice halves
+  // the texture unit's work on scales.  st_off: this lane's row in each of
+  // the wave's two load instructions (aligned byte offset, or kOOB).
+  static constexpr bool kStaged = T::kDt == kFp4 || T::kFp6;
+  // Bytes of one staging buffer: a 16-byte chunk of each of the tile's 256 B
+  // rows and 256 A rows.
+  static constexpr int kStageBytes = 512 * 16;
+  static constexpr int kChunkStride = T::kFp6 ? 12 : 16;  // row bytes between consecutive chunks
+  uint32_t st_off[2];
   // Per block (4 x blocks, then 4 y blocks): fp8, the bytes of a group of 4
   // slices, converted into sc_nxt and copied into sc_cur before the group's
   // first slice.  fp4 and fp6 convert every slice's scales straight into
@@ -773,6 +788,29 @@ struct Kernel {
       dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rss[j >> 1], sc_off[j], (uint32_t)b, 0);
   }
 
+  // fp4, fp6: chunk c of this wave's 128 rows into staging buffer BUF (row
+  // i of the 512 at bytes 16 i: B rows 0-255, then A rows 0-255).
+  template <int BUF>
+  __device__ __forceinline__ void stage_chunk(int c) {
+    LDS_AS uint8_t *dst = slots.stage[BUF] + wave * 128 * 16;
+    // (A select on the wave-uniform operand, not rss[wave >> 1]: a dynamic
+    // index into the member array would move the kernel's state to memory.)
+    const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)(dst + i * 1024), 16, st_off[i],
+                                               (uint32_t)(kChunkStride * c), 0, 0);
+  }
+  // The chunk in staging buffer BUF of every instruction's row into dst.
+  template <int BUF>
+  __device__ __forceinline__ void fetch_chunk(u32x4 (&dst)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = j < 2 ? wave_n * 128 + 64 * j + lane : 256 + wave_m * 128 + 64 * (j - 2) + lane;
+      dst[j] = *(const LDS_AS u32x4 *)(slots.stage[BUF] + row * 16);
+    }
+  }
+
   // Mask keeping the bytes of a dword that holds scale blocks b .. b + 3 of
   // a row with kb blocks (nv = kb - b of them valid).
   __device__ static __forceinline__ uint32_t keep_mask(int nv) {
@@ -786,7 +824,12 @@ struct Kernel {
   // been converted, chunk t / 2 is done with and chunk t / 2 + 2 is loaded
   // into its buffer, so no register is ever copied to another: a copy at the
   // loop's back edge waited for that load (18% of the cycles).
-  template <bool ODD, int CUR, int DST>
+  // The chunk after the next arrives from the staging buffers: at the odd
+  // slice t = 2 c + 1, chunk c + 2 (staged at slice 2 c - 1) is read into
+  // the buffer chunk c leaves, and chunk c + 3 is staged into the LDS buffer
+  // chunk c + 1 was read from (at slice 2 c - 1: every wave has passed two
+  // barriers since).  PAR = c % 2.
+  template <bool ODD, int CUR, int DST, int PAR = 0>
   __device__ __forceinline__ void convert_scales4(int t) {
     const uint32_t keep0 = keep_mask(a.kb - 8 * t), keep1 = keep_mask(a.kb - 8 * t - 4);
     u32x4(&cur)[4] = CUR == 0 ? sc_ck : sc_ckn;
@@ -806,7 +849,10 @@ struct Kernel {
       sc_set[DST][2 * j] = (int)sw[0];
       sc_set[DST][2 * j + 1] = (int)sw[1];
     }
-    if constexpr (ODD) load_chunks(cur, t / 2 + 2);
+    if constexpr (ODD) {
+      fetch_chunk<PAR>(cur);
+      stage_chunk<1 - PAR>(t / 2 + 3);
+    }
   }
 
   // fp8: group g, shifted out of the window's first two dwords and
@@ -839,7 +885,11 @@ struct Kernel {
   // groups 1, 3, in byte s.  After a chunk's last slice the next chunk
   // moves up and the one after it is loaded (three slices ahead of use).
   // Into sc_set[POS], the set slice t (in slot POS) reads.
-  template <int POS>
+  // At the chunk's last slice (POS 2, t = 3 c + 2) chunk c + 1, staged at
+  // slice 3 c - 1, is read into sc_ck from its staging buffer, and chunk
+  // c + 2 is staged into the buffer chunk c was read from (at slice 3 c - 1:
+  // every wave has passed three barriers since).  PAR = c % 2.
+  template <int POS, int PAR = 0>
   __device__ __forceinline__ void convert_scales6(int t) {
     const uint32_t keep = keep_mask(a.kb - 4 * t);
 #pragma unroll
@@ -852,9 +902,8 @@ struct Kernel {
       sc_set[POS][2 * j + 1] = (int)sw[1];
     }
     if constexpr (POS == 2) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc_ck[j] = sc_ckn[j];
-      load_bytes16(sc_ckn, 12 * (t / 3 + 2));
+      fetch_chunk<1 - PAR>(sc_ck);
+      stage_chunk<PAR>(t / 3 + 2);
     }
   }
 
@@ -897,8 +946,12 @@ struct Kernel {
       // sc_ck, 4 i + 4 and 4 i + 5 sc_ckn).  An odd slice ends its chunk,
       // whose buffer then takes the chunk after the next (waited for by the
       // next barrier, used after the one after).
-      if constexpr (T::kFp6) convert_scales6<(S + 1) % 3>(kt + 1);
-      if constexpr (T::kDt == kFp4) convert_scales4<(JB & 1) == 0, JB == 1 || JB == 2 ? 0 : 1, (JB + 1) & 1>(kt + 1);
+      // fp6: JB = kt % 6, so the chunk of slice kt + 1 (when it is a
+      // chunk's last, kt = 3 c + 1) has parity JB >= 3.  fp4: JB = kt % 4,
+      // the odd slice kt + 1 = 2 c + 1 has c % 2 = JB / 2.
+      if constexpr (T::kFp6) convert_scales6<(S + 1) % 3, JB >= 3 ? 1 : 0>(kt + 1);
+      if constexpr (T::kDt == kFp4)
+        convert_scales4<(JB & 1) == 0, JB == 1 || JB == 2 ? 0 : 1, (JB + 1) & 1, (JB >> 1) & 1>(kt + 1);
     }
     if constexpr (Q < kNRead) read_piece<S, Q>(f1, 1);
     if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNRead) read_piece<(S + 1) % kNS, Q - kBarrierAt>(f0, 0);
@@ -1017,6 +1070,16 @@ struct Kernel {
           sc_off[j] = r < rows_valid ? (pos & ~3u) : kOOB;
           sc_sh[j] = pos & 3;
         }
+        if constexpr (kStaged) {
+          if (op == (wave >> 1)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int r = (wave & 1) * 128 + 64 * i + lane;
+              const uint32_t pos = mis + (uint32_t)r * (uint32_t)a.kb;
+              st_off[i] = r < rows_valid ? (pos & ~3u) : kOOB;
+            }
+          }
+        }
       }
 #pragma unroll
       for (int i = 0; i < kNBn; ++i)
@@ -1028,12 +1091,9 @@ struct Kernel {
     // of slice 1 that a previous slice's tail would have issued; wait for
     // all but those, and convert slice 0's scales.  (With K = 0 every slice
     // is all zeros.)
-    if constexpr (T::kFp6) {
-      load_bytes16(sc_ck, 0);
-      load_bytes16(sc_ckn, 12);
-    } else if constexpr (T::kDt == kFp4) {
-      load_chunks(sc_ckn, 0);
-      load_chunks(sc_ck, 1);
+    if constexpr (kStaged) {
+      stage_chunk<0>(0);
+      stage_chunk<1>(1);
     } else if constexpr (T::kScaled) {
       load_chunks(sc_ck, 0);
       load_chunks(sc_ckn, 1);
@@ -1043,6 +1103,16 @@ struct Kernel {
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) load_one<kNS - 1>(kNS - 1, i);
     wait_vm_lgkm0<(kNS - 2) * kLoads + kTailLoads>();
+    if constexpr (kStaged) {
+      // Every wave's staged chunks 0 and 1 are in LDS after this barrier.
+      barrier();
+      if constexpr (T::kFp6) {
+        fetch_chunk<0>(sc_ck);
+      } else {
+        fetch_chunk<0>(sc_ckn);
+        fetch_chunk<1>(sc_ck);
+      }
+    }
     if constexpr (kZeroTail)
       if (zt == 0) zero_tail<0>(0);
     if constexpr (T::kDt == kFp8) {
@@ -1055,6 +1125,9 @@ struct Kernel {
       convert_scales4<false, 1, 0>(0);
     }
     barrier();
+    // fp4: chunk 2 into the buffer chunk 0 was read from (every wave's reads
+    // of it have completed before the barrier above).
+    if constexpr (T::kDt == kFp4) stage_chunk<0>(2);
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
     // Slice 0 starts the accumulators; then the slices go round the ring a
@@ -1074,14 +1147,22 @@ struct Kernel {
       if (kt + 1 < nk) step<0, 2>(kt + 1, f0, f1);
       if (kt + 2 < nk) step<1, 3>(kt + 2, f0, f1);
     } else if constexpr (kNS == 3) {
+      // Rounds of six slices: two of the three-slot ring, and two scale
+      // chunks, so that every slot and staging buffer is static.
       int kt = 1;
-      for (; kt + 2 < nk; kt += 3) {
+      for (; kt + 5 < nk; kt += 6) {
         step<1, 1>(kt, f0, f1);
         step<2, 2>(kt + 1, f0, f1);
-        step<0, 0>(kt + 2, f0, f1);
+        step<0, 3>(kt + 2, f0, f1);
+        step<1, 4>(kt + 3, f0, f1);
+        step<2, 5>(kt + 4, f0, f1);
+        step<0, 0>(kt + 5, f0, f1);
       }
       if (kt < nk) step<1, 1>(kt, f0, f1);
       if (kt + 1 < nk) step<2, 2>(kt + 1, f0, f1);
+      if (kt + 2 < nk) step<0, 3>(kt + 2, f0, f1);
+      if (kt + 3 < nk) step<1, 4>(kt + 3, f0, f1);
+      if (kt + 4 < nk) step<2, 5>(kt + 4, f0, f1);
     } else if constexpr (kNS == 4) {
       int kt = 1;
       for (; kt + 3 < nk; kt += 4) {
@@ -1244,7 +1325,6 @@ void gemm_kernel(const Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[TM * T::kPitch];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TN * T::kPitch];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[TN * T::kPitch];
-  __shared__ __attribute__((aligned(256))) uint8_t junk[4 * 256];
   Slots slots;
   slots.a[0] = (LDS_AS uint8_t *)sA0;
   slots.a[1] = (LDS_AS uint8_t *)sA1;
@@ -1266,7 +1346,20 @@ void gemm_kernel(const Args a) {
     slots.b[2] = (LDS_AS uint8_t *)sB2;
     slots.b[3] = (LDS_AS uint8_t *)sB3;
   }
-  slots.junk = (LDS_AS uint8_t *)junk;
+  slots.junk = nullptr;
+  if constexpr (Kernel<T, TM, TN, SPLIT>::kPfDist > 0) {
+    __shared__ __attribute__((aligned(256))) uint8_t junk[4 * 256];
+    slots.junk = (LDS_AS uint8_t *)junk;
+  }
+  slots.stage[0] = slots.stage[1] = nullptr;
+  if constexpr (Kernel<T, TM, TN, SPLIT>::kStaged) {
+    // Two arrays, not one indexed array, so the compiler can tell the
+    // buffer being read from the one being loaded.
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[Kernel<T, TM, TN, SPLIT>::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[Kernel<T, TM, TN, SPLIT>::kStageBytes];
+    slots.stage[0] = (LDS_AS uint8_t *)st0;
+    slots.stage[1] = (LDS_AS uint8_t *)st1;
+  }
   Kernel<T, TM, TN, SPLIT> k(a, slots);
   k.run();
 #endif
