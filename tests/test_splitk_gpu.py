@@ -159,3 +159,52 @@ def test_workspace_validation_on_device():
     finally:
         tg.set_tile(0, 0)
     torch.cuda.synchronize()
+
+
+def test_split_calls_replay_from_a_graph():
+    """gemm_bf16_splitk and gemm_bf16_splitk_noalloc launch kernels only (no
+    memset, no allocation), so a caller may capture them.  A captured pair
+    of calls is replayed three times, with eager work and synchronisation
+    between the replays; every replay must equal the eager results bit for
+    bit, and after A is doubled in place the outputs must double exactly."""
+    import ctypes
+    M, N, K = 512, 512, 4096
+    A, B = operands("bf16", M, N, K, seed=23, integer=False)
+    a = dev(A, "bf16")
+    b = as_stored(B, "bf16", 1)
+    need = tg.lib().tgemm_splitk_workspace_bytes(M, N, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    c1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    c2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def calls():
+        tg.gemm_splitk(a, b, splits=0, out=c1, workspace=ws)
+        s = torch.cuda.current_stream().cuda_stream
+        rc = tg.lib().gemm_bf16_splitk_noalloc(0, 1, M, N, K, a.data_ptr(), K, b.data_ptr(), K, c2.data_ptr(), N, 0,
+                                               ctypes.c_void_p(s))
+        assert rc == tg.OK, tg.last_error()
+
+    print(f"[gpu] splitk graph M={M} N={N} K={K}", flush=True)
+    calls()
+    torch.cuda.synchronize()
+    eager1, eager2 = to_bits(c1), to_bits(c2)
+    assert np.array_equal(eager1, eager2)
+    check("bf16", eager1, reference("bf16", A, B), False, "eager split")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        c1.fill_(0)
+        c2.fill_(0)
+        if rep == 2:
+            a.mul_(2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want1 = eager1 if rep < 2 else to_bits((torch.from_numpy(eager1.view(np.int16)).view(torch.bfloat16)
+                                                 .float() * 2).to(torch.bfloat16))
+        assert np.array_equal(to_bits(c1), want1), f"replay {rep}: gemm_bf16_splitk"
+        assert np.array_equal(to_bits(c2), want1), f"replay {rep}: gemm_bf16_splitk_noalloc"
