@@ -1221,7 +1221,9 @@ struct Kernel {
 #pragma unroll
       for (int i = 0; i < kNBn; ++i) {
         const int n = n0 + wave_n * kWN + i * kBlk + 4 * q;
-        if (m < a.M && n < a.N) *(f32x4 *)(plane + (size_t)m * a.N + n) = acc[i][j];
+        // Written through like C (the reduction reads them from another
+        // kernel): 512 x 512 x 4096 split 4 ways, 10.40 -> 9.98 us per call.
+        if (m < a.M && n < a.N) store_c((uint8_t *)(plane + (size_t)m * a.N + n), __builtin_bit_cast(u32x4, acc[i][j]));
       }
     }
   }
