@@ -381,7 +381,7 @@ struct Slots {
   LDS_AS uint8_t *a[4];
   LDS_AS uint8_t *b[4];
   LDS_AS uint8_t *junk;      // 256 bytes per wave: landing area of the L2 prefetches
-  LDS_AS uint8_t *stage[2];  // fp4, fp6: two buffers of one 16-byte scale chunk for each of the 512 rows
+  LDS_AS uint8_t *stage;     // fp4, fp6: two 16-byte scale chunks for each of the 512 rows
 };
 
 
@@ -521,19 +521,24 @@ struct Kernel {
   uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
   u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction (fp6: chunk c only)
-  // fp4, fp6: a scale chunk of every row of the tile is loaded into LDS once
-  // per workgroup (waves 0-1 the B rows, waves 2-3 the A rows, 64 rows per
-  // load instruction) and each wave then reads the rows its MFMAs take (every
-  // row feeds two waves).  The per-lane loads from global memory touch one
-  // cache line per lane, so loading each row once instead of twice halves
-  // the texture unit's work on scales.  st_off: this lane's row in each of
-  // the wave's two load instructions (aligned byte offset, or kOOB).
+  // fp4, fp6: the scale chunks of every row of the tile are loaded into LDS
+  // once per workgroup, two consecutive chunks of a row at a time (a
+  // "group": chunks 2 g and 2 g + 1; waves 0-1 the B rows, waves 2-3 the A
+  // rows), and each wave then reads the rows its MFMAs take (every row feeds
+  // two waves).  A load instruction takes 32 rows, lanes l and l + 32 the two
+  // chunks of row l, so it touches 32 cache lines for 1 KiB.  (Loading each
+  // wave's rows itself took 64 rows per instruction, one line per lane, and
+  // every row twice; one chunk of 64 rows per instruction, 64 lines, cost
+  // twice the line fetches of this for the same bytes.)  st_off: this lane's
+  // row and chunk in the wave's first load instruction (aligned byte offset,
+  // or kOOB); the other three are 32, 64 and 96 rows further, by soffset.
   static constexpr bool kStaged = T::kDt == kFp4 || T::kFp6;
-  // Bytes of one staging buffer: a 16-byte chunk of each of the tile's 256 B
-  // rows and 256 A rows.
-  static constexpr int kStageBytes = 512 * 16;
+  // Bytes of the staging buffer: two 16-byte chunks of each of the tile's
+  // 256 B rows and 256 A rows.  Instruction i of wave w fills 1 KiB block
+  // 4 w + i: chunk q of row 32 i + r of the wave's 128 at bytes 512 q + 16 r.
+  static constexpr int kStageBytes = 512 * 32;
   static constexpr int kChunkStride = T::kFp6 ? 12 : 16;  // row bytes between consecutive chunks
-  uint32_t st_off[2];
+  uint32_t st_off;
   // Per block (4 x blocks, then 4 y blocks): fp8, the bytes of a group of 4
   // slices, converted into sc_nxt and copied into sc_cur before the group's
   // first slice.  fp4 and fp6 convert every slice's scales straight into
@@ -803,26 +808,27 @@ struct Kernel {
       dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rss[j >> 1], sc_off[j], (uint32_t)b, 0);
   }
 
-  // fp4, fp6: chunk c of this wave's 128 rows into staging buffer BUF (row
-  // i of the 512 at bytes 16 i: B rows 0-255, then A rows 0-255).
-  template <int BUF>
-  __device__ __forceinline__ void stage_chunk(int c) {
-    LDS_AS uint8_t *dst = slots.stage[BUF] + wave * 128 * 16;
+  // fp4, fp6: group g (chunks 2 g and 2 g + 1) of this wave's 128 rows into
+  // the staging buffer.
+  __device__ __forceinline__ void stage_group(int g) {
+    LDS_AS uint8_t *dst = slots.stage + wave * 4 * 1024;
     // (A select on the wave-uniform operand, not rss[wave >> 1]: a dynamic
     // index into the member array would move the kernel's state to memory.)
     const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)(dst + i * 1024), 16, st_off[i],
-                                               (uint32_t)(kChunkStride * c), 0, 0);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)(dst + i * 1024), 16, st_off,
+                                               (uint32_t)(2 * kChunkStride * g + 32 * i * a.kb), 0, 0);
   }
-  // The chunk in staging buffer BUF of every instruction's row into dst.
-  template <int BUF>
+  // Chunk Q of the staged group for every instruction's row into dst: 64
+  // consecutive rows, two 512-byte runs (conflict-free 16-byte reads).
+  template <int Q>
   __device__ __forceinline__ void fetch_chunk(u32x4 (&dst)[4]) {
+    const int lp = (lane >> 5) * 1024 + (lane & 31) * 16 + Q * 512;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = j < 2 ? wave_n * 128 + 64 * j + lane : 256 + wave_m * 128 + 64 * (j - 2) + lane;
-      dst[j] = *(const LDS_AS u32x4 *)(slots.stage[BUF] + row * 16);
+      const int blk = j < 2 ? wave_n * 4 + 2 * j : 8 + wave_m * 4 + 2 * (j - 2);
+      dst[j] = *(const LDS_AS u32x4 *)(slots.stage + blk * 1024 + lp);
     }
   }
 
@@ -839,11 +845,12 @@ struct Kernel {
   // been converted, chunk t / 2 is done with and chunk t / 2 + 2 is loaded
   // into its buffer, so no register is ever copied to another: a copy at the
   // loop's back edge waited for that load (18% of the cycles).
-  // The chunk after the next arrives from the staging buffers: at the odd
-  // slice t = 2 c + 1, chunk c + 2 (staged at slice 2 c - 1) is read into
-  // the buffer chunk c leaves, and chunk c + 3 is staged into the LDS buffer
-  // chunk c + 1 was read from (at slice 2 c - 1: every wave has passed two
-  // barriers since).  PAR = c % 2.
+  // The chunk after the next arrives from the staging buffer: at the odd
+  // slice t = 2 c + 1 (converted in slice 2 c), chunk c + 2, chunk PAR = c %
+  // 2 of the staged group, is read into the buffer chunk c leaves.  Group
+  // g + 2 is staged when slice 4 g + 4 is converted, in slice 4 g + 3: the
+  // last read of group g + 1 (chunk 2 g + 3, in slice 4 g + 2) lies behind a
+  // barrier, and the group's first read (slice 4 g + 4) behind the next.
   template <bool ODD, int CUR, int DST, int PAR = 0>
   __device__ __forceinline__ void convert_scales4(int t) {
     const uint32_t keep0 = keep_mask(a.kb - 8 * t), keep1 = keep_mask(a.kb - 8 * t - 4);
@@ -864,10 +871,10 @@ struct Kernel {
       sc_set[DST][2 * j] = (int)sw[0];
       sc_set[DST][2 * j + 1] = (int)sw[1];
     }
-    if constexpr (ODD) {
+    if constexpr (ODD)
       fetch_chunk<PAR>(cur);
-      stage_chunk<1 - PAR>(t / 2 + 3);
-    }
+    else if constexpr (PAR == 1)
+      stage_group(t / 4 + 1);
   }
 
   // fp8: group g, shifted out of the window's first two dwords and
@@ -900,10 +907,12 @@ struct Kernel {
   // groups 1, 3, in byte s.  After a chunk's last slice the next chunk
   // moves up and the one after it is loaded (three slices ahead of use).
   // Into sc_set[POS], the set slice t (in slot POS) reads.
-  // At the chunk's last slice (POS 2, t = 3 c + 2) chunk c + 1, staged at
-  // slice 3 c - 1, is read into sc_ck from its staging buffer, and chunk
-  // c + 2 is staged into the buffer chunk c was read from (at slice 3 c - 1:
-  // every wave has passed three barriers since).  PAR = c % 2.
+  // At the chunk's last slice (POS 2, t = 3 c + 2, converted in slice 3 c +
+  // 1) chunk c + 1, chunk 1 - PAR of the staged group (PAR = c % 2), is read
+  // into sc_ck.  Group g + 1 is staged when slice 6 g + 3 is converted (POS
+  // 0, PAR 0), in slice 6 g + 2: the last read of group g (chunk 2 g + 1, in
+  // slice 6 g + 1) lies behind a barrier, and the group's first read (chunk
+  // 2 g + 2, in slice 6 g + 4) behind the next.
   template <int POS, int PAR = 0>
   __device__ __forceinline__ void convert_scales6(int t) {
     const uint32_t keep = keep_mask(a.kb - 4 * t);
@@ -916,10 +925,10 @@ struct Kernel {
       sc_set[POS][2 * j] = (int)sw[0];
       sc_set[POS][2 * j + 1] = (int)sw[1];
     }
-    if constexpr (POS == 2) {
+    if constexpr (POS == 2)
       fetch_chunk<1 - PAR>(sc_ck);
-      stage_chunk<PAR>(t / 3 + 2);
-    }
+    else if constexpr (POS == 0 && PAR == 0)
+      stage_group(t / 6 + 1);
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
@@ -1087,12 +1096,11 @@ struct Kernel {
         }
         if constexpr (kStaged) {
           if (op == (wave >> 1)) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-              const int r = (wave & 1) * 128 + 64 * i + lane;
-              const uint32_t pos = mis + (uint32_t)r * (uint32_t)a.kb;
-              st_off[i] = r < rows_valid ? (pos & ~3u) : kOOB;
-            }
+            // Rows r + 32, r + 64, r + 96 are 32 kb bytes apart each, and so
+            // are their aligned offsets.
+            const int r = (wave & 1) * 128 + (lane & 31);
+            const uint32_t pos = mis + (uint32_t)r * (uint32_t)a.kb;
+            st_off = r < rows_valid ? (pos & ~3u) + (uint32_t)(kChunkStride * (lane >> 5)) : kOOB;
           }
         }
       }
@@ -1107,8 +1115,7 @@ struct Kernel {
     // all but those, and convert slice 0's scales.  (With K = 0 every slice
     // is all zeros.)
     if constexpr (kStaged) {
-      stage_chunk<0>(0);
-      stage_chunk<1>(1);
+      stage_group(0);
     } else if constexpr (T::kScaled) {
       load_chunks(sc_ck, 0);
       load_chunks(sc_ckn, 1);
@@ -1119,7 +1126,7 @@ struct Kernel {
     for (int i = 0; i < kTailLoads; ++i) load_one<kNS - 1>(kNS - 1, i);
     wait_vm_lgkm0<(kNS - 2) * kLoads + kTailLoads>();
     if constexpr (kStaged) {
-      // Every wave's staged chunks 0 and 1 are in LDS after this barrier.
+      // Every wave's staged group 0 is in LDS after this barrier.
       barrier();
       if constexpr (T::kFp6) {
         fetch_chunk<0>(sc_ck);
@@ -1135,14 +1142,15 @@ struct Kernel {
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
     } else if constexpr (T::kFp6) {
-      convert_scales6<0>(0);
+      // (PAR 1: group 1 is staged in slice 2, after chunk 1 has been read.)
+      convert_scales6<0, 1>(0);
     } else if constexpr (T::kDt == kFp4) {
       convert_scales4<false, 1, 0>(0);
     }
     barrier();
-    // fp4: chunk 2 into the buffer chunk 0 was read from (every wave's reads
-    // of it have completed before the barrier above).
-    if constexpr (T::kDt == kFp4) stage_chunk<0>(2);
+    // fp4: group 1 (chunks 2 and 3) over group 0, whose reads by every wave
+    // have completed before the barrier above.
+    if constexpr (T::kDt == kFp4) stage_group(1);
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
     // Slice 0 starts the accumulators; then the slices go round the ring a
@@ -1368,14 +1376,10 @@ void gemm_kernel(const Args a) {
     __shared__ __attribute__((aligned(256))) uint8_t junk[4 * 256];
     slots.junk = (LDS_AS uint8_t *)junk;
   }
-  slots.stage[0] = slots.stage[1] = nullptr;
+  slots.stage = nullptr;
   if constexpr (Kernel<T, TM, TN, SPLIT>::kStaged) {
-    // Two arrays, not one indexed array, so the compiler can tell the
-    // buffer being read from the one being loaded.
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[Kernel<T, TM, TN, SPLIT>::kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[Kernel<T, TM, TN, SPLIT>::kStageBytes];
-    slots.stage[0] = (LDS_AS uint8_t *)st0;
-    slots.stage[1] = (LDS_AS uint8_t *)st1;
+    __shared__ __attribute__((aligned(1024))) uint8_t st[Kernel<T, TM, TN, SPLIT>::kStageBytes];
+    slots.stage = (LDS_AS uint8_t *)st;
   }
   Kernel<T, TM, TN, SPLIT> k(a, slots);
   k.run();
