@@ -104,7 +104,8 @@ struct Args {
 // fp4 operands are handled as rows of bytes (two E2M1 elements each):
 // kElem = 1 and K counts bytes inside the kernel.
 // fp6 (E2M3 or E3M2) likewise: rows of densely packed 6-bit elements, K
-// counted in bytes, 96 bytes (128 elements, two MFMA K steps) per slice.
+// counted in bytes; its K loop runs 64-element steps over 128-byte line
+// stages (the kernel's fp6 section).
 enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2, kFp4 = 3, kFp6E2M3 = 4, kFp6E3M2 = 5 };
 template <int DT, bool AK, bool BK, bool WHOLE = false>
 struct Traits {
@@ -116,8 +117,8 @@ struct Traits {
   static constexpr bool kScaled = DT >= kFp8;
   static constexpr bool kFp6 = DT == kFp6E2M3 || DT == kFp6E3M2;
   static constexpr int kElem = kScaled ? 1 : 2;
-  static constexpr int kSliceBytes = kFp6 ? 96 : 128;  // global bytes of a row per K slice
-  static constexpr int kPitch = kSliceBytes;               // LDS bytes of a slot row
+  static constexpr int kSliceBytes = 128;                  // global bytes of a row per K slice (fp6: line stage)
+  static constexpr int kPitch = kFp6 ? 144 : kSliceBytes;  // LDS bytes of a slot row
   static constexpr bool kAK = AK, kBK = BK;
 };
 
@@ -282,46 +283,6 @@ struct PanelLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Staging of one K slice of a K-contiguous fp6 panel (96 bytes of each of
-// 64 NI / 6 rows) into a slot of 96-byte rows, packed densely.  Wave w moves
-// 16-byte pieces [64 NI w, 64 NI (w + 1)) of the slot with NI direct-to-LDS
-// instructions; lane l of instruction i writes piece p = 64 (NI w + i) + l,
-// i.e. row p / 6, physical chunk p % 6, and so fetches the logical chunk
-// stored there: a row r keeps logical chunk c at physical chunk
-// (c + rot6(r)) % 6.  With rot6(r) = (r >> 3) & 3 the fragment reads (32
-// rows, one 8-byte piece each) meet at most two to a bank pair, the least
-// that 96-byte rows allow.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int rot6(int r) { return (r >> 3) & 3; }
-
-template <int NI>
-struct DenseLoader {
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[NI];  // per instruction: byte offset of this lane's chunk at slice 0, or kOOB
-  uint32_t chunks;   // logical chunk of instruction i in bits 3 i .. 3 i + 2
-
-  __device__ __forceinline__ void init(const uint8_t *panel, int rows_valid, int K, int ld, int wave, int lane) {
-    static_assert(3 * NI <= 32, "chunk indices packed in one register");
-    rsrc = make_rsrc(panel, (uint32_t)(rows_valid - 1) * (uint32_t)ld + (uint32_t)K);
-    chunks = 0;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int p = (wave * NI + i) * 64 + lane;
-      const int r = p / 6, c = (p - 6 * r + 6 - rot6(r)) % 6;
-      chunks |= (uint32_t)c << (3 * i);
-      off[i] = r < rows_valid ? (uint32_t)r * (uint32_t)ld + 16u * (uint32_t)c : kOOB;
-    }
-  }
-
-  // Instruction i of slice kt; a chunk at or past byte K loads nothing.
-  __device__ __forceinline__ void issue(LDS_AS uint8_t *slot, int wave, int kt, int K, int slice_k, int i) const {
-    const bool ok = kt * slice_k + 16 * (int)((chunks >> (3 * i)) & 7u) < K;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(slot + (wave * NI + i) * 1024), 16,
-                                             ok ? off[i] : kOOB, (uint32_t)(kt * slice_k), 0, 0);
-  }
-};
-
-// ---------------------------------------------------------------------------
 // Staging of one K slice of an M- or N-contiguous 16-bit operand (A stored
 // K x M, B stored K x N, rows ld elements apart) for a tile of W columns
 // (W = 256 or 128) into a slot of 64 K rows x 2 W bytes.  Wave w moves K
@@ -369,13 +330,12 @@ struct MNLoader {
 // The kernel.
 // ---------------------------------------------------------------------------
 // LDS slots of the K-slice ring.  The 256-row tiles fill the LDS with two
-// (2 x 64 KiB); fp6's 96-byte rows leave room for three (3 x 48 KiB),
-// which its short slices (1056 MFMA cycles) need.  A 128 x 128 tile's slice holds a quarter of the MFMA work
+// (2 x 64 KiB; fp6: 2 x 72 KiB of 144-byte rows).  A 128 x 128 tile's slice holds a quarter of the MFMA work
 // of a 256 x 256 one, too little to cover the latency of the next slice's
 // loads with one slice in flight, so its ring has four slots (4 x 32 KiB):
 // the loads of slice kt + 4 go out in slice kt, three slices ahead of use.
 template <class T, int TM, int TN>
-constexpr int kSlots = T::kFp6 ? 3 : (!T::kScaled && TM * TN <= 128 * 128) ? 4 : 2;
+constexpr int kSlots = (!T::kScaled && TM * TN <= 128 * 128) ? 4 : 2;
 
 struct Slots {
   LDS_AS uint8_t *a[4];
@@ -408,9 +368,9 @@ struct Kernel {
   static constexpr int kHalves = T::kDt == kFp4 ? 2 : 1;
   static constexpr int kPerSub = kNBm * kNBn * kHalves;  // MFMAs per substep
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
-  // Load instructions per wave per slice: 8 rows of 128 bytes each, or (fp6)
-  // 64 pieces of 16 bytes of the dense slot.
-  static constexpr int kLA = T::kFp6 ? TM * 6 / 256 : TM / 32, kLB = T::kFp6 ? TN * 6 / 256 : TN / 32;
+  // Load instructions per wave per slice: 8 rows of 128 bytes each (fp6 has
+  // its own K loop, below).
+  static constexpr int kLA = TM / 32, kLB = TN / 32;
   static constexpr int kLoads = kLA + kLB;
   static_assert(!T::kScaled || (TM == 256 && TN == 256 && T::kAK && T::kBK),
                 "the block-scaled kernel uses 256 x 256 tiles of K-contiguous operands");
@@ -449,7 +409,7 @@ struct Kernel {
   static constexpr int kLastLoad = kFreeAt + (kLoads - 1) * kWindow / kLoads;
   static constexpr bool kPfHead = kLastLoad >= kMfma;  // last load in the next slice's head
   static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
-  // (Not for fp6: its three-slot ring already loads slice kt + 3 in slice kt.)
+  // (Not for fp6, which has its own K loop.)
   static constexpr int kPfDist = T::kScaled && !T::kFp6 ? 3 : 0;
   static_assert(kPfDist == 0 || !kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
   static_assert(kPfDist == 0 || kPfHead || kPfAt < kMfma, "prefetch position");
@@ -488,13 +448,11 @@ struct Kernel {
   int tid, lane, wave, wave_m, wave_n, lane_sw;
   int m0, n0;
   int nk;
-  int kK;  // K of this workgroup's range (all of K unless split)
+  int kK;     // K of this workgroup's range (all of K unless split)
+  int split;  // K split: this workgroup's range
   int zt;  // the ragged last slice (or the only, all-zero one when K = 0); -1 if none
-  typename std::conditional<T::kFp6, DenseLoader<kLA>,
-                            typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type>::type la;
-  typename std::conditional<T::kFp6, DenseLoader<kLB>,
-                            typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type>::type lb;
-  int f6off[6];  // fp6: byte offset of this lane's 8-byte pieces (K step s, piece q at 3 s + q) in a block
+  typename std::conditional<T::kAK, PanelLoader<kLA>, MNLoader<TM>>::type la;
+  typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type lb;
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
   // Block scales.  Each lane streams the scale bytes of one row per
@@ -520,7 +478,7 @@ struct Kernel {
   __amdgpu_buffer_rsrc_t rss[2];  // B scales, A scales; based at the tile's first row, dword aligned
   uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
-  u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction (fp6: chunk c only)
+  u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction (fp6: chunks 2 p and 2 p + 1 of round p)
   // fp4, fp6: the scale chunks of every row of the tile are loaded into LDS
   // once per workgroup, two consecutive chunks of a row at a time (a
   // "group": chunks 2 g and 2 g + 1; waves 0-1 the B rows, waves 2-3 the A
@@ -537,15 +495,15 @@ struct Kernel {
   // 256 B rows and 256 A rows.  Instruction i of wave w fills 1 KiB block
   // 4 w + i: chunk q of row 32 i + r of the wave's 128 at bytes 512 q + 16 r.
   static constexpr int kStageBytes = 512 * 32;
-  static constexpr int kChunkStride = T::kFp6 ? 12 : 16;  // row bytes between consecutive chunks
+  static constexpr int kChunkStride = 16;  // row bytes between consecutive chunks
   uint32_t st_off;
   // Per block (4 x blocks, then 4 y blocks): fp8, the bytes of a group of 4
   // slices, converted into sc_nxt and copied into sc_cur before the group's
   // first slice.  fp4 and fp6 convert every slice's scales straight into
-  // the set its MFMAs read (fp4: set kt % 2, fp6: set kt % 3, the slot), so
-  // no copy is needed at the start of a slice.
+  // the set its MFMAs read (fp4: set kt % 2; fp6: set (k / 2) % 2 for K step
+  // k), so no copy is needed at the start of a slice.
   int sc_nxt[8], sc_cur[8];
-  int sc_set[3][8];
+  int sc_set[2][8];
   Acc acc[kNBn][kNBm];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
@@ -553,20 +511,7 @@ struct Kernel {
   // Fragment of one block of kBlk rows (B rows = C columns for x, A rows for
   // y), K substep `sub`, from a K-contiguous slot.
   __device__ __forceinline__ Frag read_rows(const LDS_AS uint8_t *slot, int row0, int sub) const {
-    if constexpr (T::kFp6) {
-      // 32 x 32 x 64 on fp6: lane l holds row l % 32 and 24 bytes (32
-      // elements) of K: bytes 48 sub + 24 (l / 32) .. + 23, three 8-byte
-      // pieces at the offsets set up in run().
-      const LDS_AS uint8_t *p = slot + row0 * T::kPitch;
-      i32x6 r;
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const u32x2 v = *(const LDS_AS u32x2 *)(p + f6off[3 * sub + q]);
-        r[2 * q] = (int)v[0];
-        r[2 * q + 1] = (int)v[1];
-      }
-      return r;
-    } else if constexpr (kW) {
+    if constexpr (kW) {
       // 32 x 32 x 64: lane l holds row l % 32 and 32 bytes of K: logical
       // chunks 4 sub + 2 (l / 32) and the one after.
       const int c = 4 * sub + 2 * (lane >> 5);
@@ -757,18 +702,14 @@ struct Kernel {
   template <int S>
   __device__ __forceinline__ void load_one(int kt, int i) {
     if (i < kLA) {
-      if constexpr (T::kFp6)
-        la.issue(slots.a[S], wave, kt, kK, kSliceK, i);
-      else if constexpr (T::kScaled && !T::kWholeK)
+      if constexpr (T::kScaled && !T::kWholeK)
         la.issue_masked(slots.a[S], wave, kt, kK, kSliceK, i);
       else if constexpr (T::kAK)
         la.issue(slots.a[S], wave, kt, i);
       else
         la.issue(slots.a[S], wave, kt, nk, i);
     } else {
-      if constexpr (T::kFp6)
-        lb.issue(slots.b[S], wave, kt, kK, kSliceK, i - kLA);
-      else if constexpr (T::kScaled && !T::kWholeK)
+      if constexpr (T::kScaled && !T::kWholeK)
         lb.issue_masked(slots.b[S], wave, kt, kK, kSliceK, i - kLA);
       else if constexpr (T::kBK)
         lb.issue(slots.b[S], wave, kt, i - kLA);
@@ -784,8 +725,8 @@ struct Kernel {
   static constexpr bool kZeroTail = !T::kScaled && (T::kAK || T::kBK);
   template <int S>
   __device__ __forceinline__ void zero_tail(int kt) {
-    if constexpr (T::kAK && !T::kFp6) la.zero_tail(slots.a[S], wave, lane, kt, kK, kSliceK);
-    if constexpr (T::kBK && !T::kFp6) lb.zero_tail(slots.b[S], wave, lane, kt, kK, kSliceK);
+    if constexpr (T::kAK) la.zero_tail(slots.a[S], wave, lane, kt, kK, kSliceK);
+    if constexpr (T::kBK) lb.zero_tail(slots.b[S], wave, lane, kt, kK, kSliceK);
     wait_vm_lgkm0<63>();
   }
 
@@ -898,39 +839,6 @@ struct Kernel {
     if ((g & 3) == 3) load_chunks(sc_ckn, (g >> 2) + 2);
   }
 
-  // fp6: slice t's 4 scale bytes per row (groups 0-3 of its 128 elements).
-  // Its chunks are 16 bytes every 12 (slices 3 c .. 3 c + 2 and the bytes
-  // an unaligned row start shifts in), so slice t = 3 c + POS is dwords POS
-  // and POS + 1 of chunk c: with slice kt in slot kt % 3, POS is fixed for
-  // every step, and no index is dynamic.  The MFMA of K step s in wave half
-  // w uses group 2 s + w, so lanes 0-31 take groups 0, 2 and lanes 32-63
-  // groups 1, 3, in byte s.  After a chunk's last slice the next chunk
-  // moves up and the one after it is loaded (three slices ahead of use).
-  // Into sc_set[POS], the set slice t (in slot POS) reads.
-  // At the chunk's last slice (POS 2, t = 3 c + 2, converted in slice 3 c +
-  // 1) chunk c + 1, chunk 1 - PAR of the staged group (PAR = c % 2), is read
-  // into sc_ck.  Group g + 1 is staged when slice 6 g + 3 is converted (POS
-  // 0, PAR 0), in slice 6 g + 2: the last read of group g (chunk 2 g + 1, in
-  // slice 6 g + 1) lies behind a barrier, and the group's first read (chunk
-  // 2 g + 2, in slice 6 g + 4) behind the next.
-  template <int POS, int PAR = 0>
-  __device__ __forceinline__ void convert_scales6(int t) {
-    const uint32_t keep = keep_mask(a.kb - 4 * t);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t d = __builtin_amdgcn_alignbyte(sc_ck[j][POS + 1], sc_ck[j][POS], sc_sh[j]) & keep;
-      const uint32_t lo = __builtin_amdgcn_perm(0u, d, 0x0c0c0200u);  // groups 0, 2
-      const uint32_t hi = __builtin_amdgcn_perm(0u, d, 0x0c0c0301u);  // groups 1, 3
-      const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
-      sc_set[POS][2 * j] = (int)sw[0];
-      sc_set[POS][2 * j + 1] = (int)sw[1];
-    }
-    if constexpr (POS == 2)
-      fetch_chunk<1 - PAR>(sc_ck);
-    else if constexpr (POS == 0 && PAR == 0)
-      stage_group(t / 6 + 1);
-  }
-
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
   // inside it x block q / kNBm times y block q % kNBm (in reverse order
   // under odd x blocks).  Interleaved with it:
@@ -970,10 +878,7 @@ struct Kernel {
       // sc_ck, 4 i + 4 and 4 i + 5 sc_ckn).  An odd slice ends its chunk,
       // whose buffer then takes the chunk after the next (waited for by the
       // next barrier, used after the one after).
-      // fp6: JB = kt % 6, so the chunk of slice kt + 1 (when it is a
-      // chunk's last, kt = 3 c + 1) has parity JB >= 3.  fp4: JB = kt % 4,
-      // the odd slice kt + 1 = 2 c + 1 has c % 2 = JB / 2.
-      if constexpr (T::kFp6) convert_scales6<(S + 1) % 3, JB >= 3 ? 1 : 0>(kt + 1);
+      // fp4: JB = kt % 4, the odd slice kt + 1 = 2 c + 1 has c % 2 = JB / 2.
       if constexpr (T::kDt == kFp4)
         convert_scales4<(JB & 1) == 0, JB == 1 || JB == 2 ? 0 : 1, (JB + 1) & 1, (JB >> 1) & 1>(kt + 1);
     }
@@ -986,8 +891,6 @@ struct Kernel {
     if constexpr (T::kDt == kFp4)
       acc[I][J] = mma<FIRST && SUB == 0 && H == 0, 2 * SUB + H, H>(f.x[I], f.y[J], acc[I][J], sc_set[JB & 1][I],
                                                                    sc_set[JB & 1][4 + J]);
-    else if constexpr (T::kFp6)
-      acc[I][J] = mma<FIRST && SUB == 0, SUB>(f.x[I], f.y[J], acc[I][J], sc_set[S][I], sc_set[S][4 + J]);
     else if constexpr (T::kScaled)
       acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
@@ -1023,7 +926,7 @@ struct Kernel {
     int tm, tn;
     const int tiles = a.tiles_m * a.tiles_n;
     const int wg = (int)blockIdx.x;
-    const int split = SPLIT ? wg / tiles : 0;
+    split = SPLIT ? wg / tiles : 0;
     tile_of(SPLIT ? wg - split * tiles : wg, tiles, a.tiles_m, a.tiles_n, tm, tn);
     m0 = tm * TM;
     n0 = tn * TN;
@@ -1043,27 +946,17 @@ struct Kernel {
     zt = K % kSliceK != 0 || nk == 0 ? (nk > 0 ? nk - 1 : 0) : -1;
 
     if constexpr (T::kFp6)
-      la.init(a.A + (size_t)m0 * a.lda, min(a.M - m0, TM), K, a.lda, wave, lane);
+      ;  // fp6 sets up its own loads (run6)
     else if constexpr (T::kAK)
       la.init(a.A + ((size_t)m0 * a.lda + k0) * kElem, min(a.M - m0, TM), K, a.lda, kElem, kSliceK, wave, lane);
     else
       la.init(a.A + (size_t)k0 * a.lda * kElem, K, a.M, m0, a.lda, wave, lane);
     if constexpr (T::kFp6)
-      lb.init(a.B + (size_t)n0 * a.ldb, min(a.N - n0, TN), K, a.ldb, wave, lane);
+      ;
     else if constexpr (T::kBK)
       lb.init(a.B + ((size_t)n0 * a.ldb + k0) * kElem, min(a.N - n0, TN), K, a.ldb, kElem, kSliceK, wave, lane);
     else
       lb.init(a.B + (size_t)k0 * a.ldb * kElem, K, a.N, n0, a.ldb, wave, lane);
-    if constexpr (T::kFp6) {
-      // Fragment rows start at multiples of 32, so a lane's row has rot6 of
-      // lane % 32.  Logical 8-byte piece 6 s + 3 (l / 32) + q of the row.
-#pragma unroll
-      for (int sq = 0; sq < 6; ++sq) {
-        const int u = 6 * (sq / 3) + 3 * (lane >> 5) + sq % 3;
-        const int c = ((u >> 1) + rot6(lane & 31)) % 6;
-        f6off[sq] = (lane & 31) * T::kPitch + 16 * c + 8 * (u & 1);
-      }
-    }
     if constexpr (kPfDist > 0) {
       // Waves 0-1 take 32 rows of the A panel (its share among the 8 tile
       // columns of an XCD's block), waves 2-3 take 64 rows of the B panel
@@ -1109,6 +1002,15 @@ struct Kernel {
 #pragma unroll
         for (int j = 0; j < kNBm; ++j) acc[i][j] = Acc{};
     }
+    if constexpr (T::kFp6)
+      run6();
+    else
+      run_slices();
+  }
+
+  // The K loop over slices (every kind but fp6), from its prologue to the
+  // epilogue.
+  __device__ __forceinline__ void run_slices() {
 
     // Prologue: the first two scale chunks, slice 0 into slot 0, the loads
     // of slice 1 that a previous slice's tail would have issued; wait for
@@ -1128,12 +1030,8 @@ struct Kernel {
     if constexpr (kStaged) {
       // Every wave's staged group 0 is in LDS after this barrier.
       barrier();
-      if constexpr (T::kFp6) {
-        fetch_chunk<0>(sc_ck);
-      } else {
-        fetch_chunk<0>(sc_ckn);
-        fetch_chunk<1>(sc_ck);
-      }
+      fetch_chunk<0>(sc_ckn);
+      fetch_chunk<1>(sc_ck);
     }
     if constexpr (kZeroTail)
       if (zt == 0) zero_tail<0>(0);
@@ -1141,9 +1039,6 @@ struct Kernel {
       convert_scales(0);
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
-    } else if constexpr (T::kFp6) {
-      // (PAR 1: group 1 is staged in slice 2, after chunk 1 has been read.)
-      convert_scales6<0, 1>(0);
     } else if constexpr (T::kDt == kFp4) {
       convert_scales4<false, 1, 0>(0);
     }
@@ -1169,23 +1064,6 @@ struct Kernel {
       if (kt < nk) step<1, 1>(kt, f0, f1);
       if (kt + 1 < nk) step<0, 2>(kt + 1, f0, f1);
       if (kt + 2 < nk) step<1, 3>(kt + 2, f0, f1);
-    } else if constexpr (kNS == 3) {
-      // Rounds of six slices: two of the three-slot ring, and two scale
-      // chunks, so that every slot and staging buffer is static.
-      int kt = 1;
-      for (; kt + 5 < nk; kt += 6) {
-        step<1, 1>(kt, f0, f1);
-        step<2, 2>(kt + 1, f0, f1);
-        step<0, 3>(kt + 2, f0, f1);
-        step<1, 4>(kt + 3, f0, f1);
-        step<2, 5>(kt + 4, f0, f1);
-        step<0, 0>(kt + 5, f0, f1);
-      }
-      if (kt < nk) step<1, 1>(kt, f0, f1);
-      if (kt + 1 < nk) step<2, 2>(kt + 1, f0, f1);
-      if (kt + 2 < nk) step<0, 3>(kt + 2, f0, f1);
-      if (kt + 3 < nk) step<1, 4>(kt + 3, f0, f1);
-      if (kt + 4 < nk) step<2, 5>(kt + 4, f0, f1);
     } else if constexpr (kNS == 4) {
       int kt = 1;
       for (; kt + 3 < nk; kt += 4) {
@@ -1213,6 +1091,309 @@ struct Kernel {
       epilogue_partial(split);
     else
       epilogue();
+  }
+
+  // -------------------------------------------------------------------------
+  // fp6: line stages.
+  //
+  // A K step (64 elements) is 48 bytes of a row; lane l of the 32 x 32 x 64
+  // MFMA takes row l % 32 and the step's bytes 24 (l / 32) .. + 23.  Slices
+  // of two steps (96 bytes) would straddle 128-byte cache lines in half the
+  // rows, and a row's line fetched twice costs the texture path as much as
+  // two lines: 1.5 lines per row per 96 bytes.  Here the loads stage whole
+  // lines instead, stage L being row bytes 128 L .. 128 L + 127 of every
+  // row of the tile, so every byte crosses from L2 once: three stages per
+  // period of 8 K steps (384 bytes).  Two slots hold two stages; a slot row
+  // is 144 bytes (the line and 16 unused bytes), so that the 32 rows a
+  // fragment read takes meet at most two to a bank pair and every read
+  // address is a per-lane base plus a constant.
+  //
+  // Inside a period, step J (0..7) takes bytes 48 J .. 48 J + 47 of its
+  // period: steps 0, 1 lie in the period's first line (ell 0), 3, 4 in the
+  // second, 6, 7 in the third; step 2's upper half-wave needs pieces of
+  // lines 0 and 1, step 5's lower half-wave pieces of lines 1 and 2.  The
+  // fragments of step k + 1 are read during step k.  For steps 2 and 5 the
+  // pieces in the older line are read first (by the half-wave that needs
+  // them), the barrier then publishes the newer line and frees the older,
+  // and the other half-wave reads its pieces of the newer line.  Barriers,
+  // at MFMA kMB of steps 1, 4, 6 and 7:
+  //   step 1: line ell 1 has landed; ell 0's slot takes line ell 2;
+  //   step 4: ell 2 has landed; ell 1's slot takes ell 3;
+  //   step 6: ell 2's reads are done; its slot takes ell 4;
+  //   step 7: ell 3 has landed.
+  // (ell 3 and ell 4 are the next period's lines 0 and 1.)  Each line's
+  // loads go out over about two steps and have three steps from the barrier
+  // that frees its slot to the one that publishes it.  Line L sits in slot
+  // L % 2; a round of two periods (16 steps, 6 lines) makes every slot and
+  // position static.
+  //
+  // Scales: 16-byte chunks (one per 8 steps), staged two per row per round
+  // (group p: chunks 2 p, 2 p + 1); sc_ck holds chunk 2 p (read in step 6 of
+  // round p - 1), sc_ckn chunk 2 p + 1 (read in step 14 of round p - 1);
+  // group p + 2 is staged in step 15 of round p, after the last read of
+  // group p + 1.  Pair u (steps 2 u, 2 u + 1) of a round has its 4 bytes
+  // converted in step 2 u - 1 into set u % 2.
+  // -------------------------------------------------------------------------
+  static constexpr int kL6 = 9;   // load instructions per wave per operand and line (256 rows x 9 16-byte pieces / 4 waves / 64)
+  static constexpr int kMB = 8;   // MFMA of a step at which its barrier goes
+  static constexpr int kLS = 2;   // MFMAs between two load instructions of a line
+  // Period position (16 J + MFMA) of load instruction i of the lines issued
+  // in a period: ell 2 from the barrier in step 1, ell 3 from the one in
+  // step 4, ell 4 from one MFMA after the one in step 6 (odd positions, so
+  // they never meet ell 3's); ell 4's last six fall in the next period.
+  static constexpr int kPos2 = 16 * 1 + kMB, kPos3 = 16 * 4 + kMB, kPos4 = 16 * 6 + kMB + 1;
+  static_assert(kPos2 + kLS * (2 * kL6 - 1) < kPos3, "ell 2's loads end before their barrier");
+  static_assert(kPos3 + kLS * (2 * kL6 - 1) < 16 * 7 + kMB, "ell 3's loads end before their barrier");
+  static_assert(kPos4 + kLS * (2 * kL6 - 1) - 128 < 16 * 1 + kMB, "ell 4's loads end before their barrier");
+  // Loads of ell 4 issued between the last of ell 3 and the barrier of step
+  // 7 (which waits for ell 3 only).
+  static constexpr int vm_at7() {
+    const int last3 = kPos3 + kLS * (2 * kL6 - 1);
+    int n = 0;
+    for (int i = 0; i < 2 * kL6; ++i) n += kPos4 + kLS * i > last3 && kPos4 + kLS * i < 16 * 7 + kMB;
+    return n;
+  }
+
+  uint32_t l6off[kL6];             // per instruction: byte offset of this lane's piece in the panel, or kOOB
+  __amdgpu_buffer_rsrc_t rs6[2];   // the A and B panels of the tile
+  const LDS_AS uint8_t *rb[2][2];  // [slot][0: A, 1: B]: this lane's fragment row (block 0) + 24 (lane / 32)
+  const LDS_AS uint8_t *rbh[2][2]; // the same without the half-wave's 24 bytes
+
+  // Load instruction I (A: 0 .. kL6 - 1, B: kL6 ..) of line L into slot S.
+  // Past the last row the range check returns zeros; past a row's end the
+  // pieces hold the next row's bytes, which no fragment read takes.
+  template <int S, int I>
+  __device__ __forceinline__ void load6(int L) {
+    constexpr int op = I < kL6 ? 0 : 1, i = I % kL6;
+    LDS_AS uint8_t *dst = (op ? slots.b[S] : slots.a[S]) + (kL6 * wave + i) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs6[op], (LDS_AS void *)dst, 16, l6off[i], (uint32_t)(128 * L), 0, 0);
+  }
+
+  // Piece Q (bytes 8 Q .. 8 Q + 7, registers 2 Q and 2 Q + 1) of fragment R
+  // (x blocks 0-3 from B, then y blocks 0-3 from A) from slot S, at byte X
+  // of the lower half-wave's line (MODE 0: both half-waves, the upper one 24
+  // bytes further; MODE 1: for the lower half-wave) or of the upper
+  // half-wave's line (MODE 2: for the upper half-wave).
+  template <int S, int R, int Q, int MODE, int X>
+  __device__ __forceinline__ void piece6(Frags &f) {
+    constexpr int op = R < kNBn ? 1 : 0;
+    constexpr int off = (R % 4) * 32 * T::kPitch + X;
+    static_assert(X >= 0 && off < 65536, "constant LDS offset");
+    if constexpr (R < kNBn)
+      piece6_into<S, op, Q, MODE, off>(f.x[R]);
+    else
+      piece6_into<S, op, Q, MODE, off>(f.y[R - kNBn]);
+  }
+  // (MODE 1 reads for every lane, from rbh: the upper half-wave takes bytes
+  // of its own row that its MODE 2 read replaces.  MODE 2 merges with a
+  // select: a branch around the read made the compiler spill.)
+  template <int S, int OP, int Q, int MODE, int OFF>
+  __device__ __forceinline__ void piece6_into(Frag &fr) {
+    const u32x2 v = *(const LDS_AS u32x2 *)((MODE == 0 ? rb[S][OP] : rbh[S][OP]) + OFF);
+    if constexpr (MODE < 2) {
+      fr[2 * Q] = (int)v[0];
+      fr[2 * Q + 1] = (int)v[1];
+    } else {
+      const bool up = lane >= 32;
+      fr[2 * Q] = up ? (int)v[0] : fr[2 * Q];
+      fr[2 * Q + 1] = up ? (int)v[1] : fr[2 * Q + 1];
+    }
+  }
+
+  // The reads of step J's successor, in the order y0, x0, y1, y2, y3, x1,
+  // x2, x3 (the order the MFMAs first take them).  Read n of the N in a
+  // list goes out at MFMA M0 + n (M1 - M0) / N.
+  static constexpr int kFragOrder[8] = {4, 0, 5, 6, 7, 1, 2, 3};
+  struct Rd {
+    int r, q, mode, ell, x;
+  };
+  // Read n of the list of step J (period position): part 0 before the
+  // barrier, part 1 after it (steps 1 and 4), or the whole list.
+  static constexpr int n_reads(int J, int part) {
+    return J == 1 ? (part == 0 ? 24 : 16) : J == 4 ? (part == 0 ? 16 : 24) : 24;
+  }
+  static constexpr Rd read_of(int J, int part, int n) {
+    const int Jt = J + 1;  // the step read (8: the next period's step 0)
+    if (J == 1 && part == 1) {
+      const int f = kFragOrder[n / 2], q = 1 + n % 2;
+      return Rd{f, q, 2, 1, 48 * Jt + 24 + 8 * q - 128};
+    }
+    if (J == 4 && part == 0) {
+      const int f = kFragOrder[n / 2], q = n % 2;
+      return Rd{f, q, 1, 1, 48 * Jt + 8 * q - 128};
+    }
+    if (J == 4 && part == 1) {
+      const int f = kFragOrder[n / 3], q = n % 3;
+      return q < 2 ? Rd{f, q, 2, 2, 48 * Jt + 24 + 8 * q - 256} : Rd{f, 2, 0, 2, 48 * Jt + 16 - 256};
+    }
+    const int f = kFragOrder[n / 3], q = n % 3;
+    const int ell = Jt * 48 / 128;  // the line of the step's first byte
+    const int mode = J == 1 && q > 0 ? 1 : 0;
+    return Rd{f, q, mode, ell, 48 * Jt + 8 * q - 128 * ell};
+  }
+  // MFMA range of a list.
+  static constexpr int rd_m0(int J, int part) { return (J == 1 || J == 4) ? (part == 0 ? 0 : kMB) : J == 7 ? kMB : 0; }
+  static constexpr int rd_m1(int J, int part) {
+    return (J == 1 || J == 4) ? (part == 0 ? kMB : 16) : J == 6 ? kMB : 16;
+  }
+  static constexpr int rd_m(int J, int part, int n) {
+    return rd_m0(J, part) + n * (rd_m1(J, part) - rd_m0(J, part)) / n_reads(J, part);
+  }
+
+  template <int H, int J, int M, int PART, int N>
+  __device__ __forceinline__ void read_if(Frags &f) {
+    if constexpr (rd_m(J, PART, N) == M) {
+      constexpr Rd d = read_of(J, PART, N);
+      piece6<(H + d.ell) % 2, d.r, d.q, d.mode, d.x>(f);
+    }
+  }
+  template <int H, int J, int M, int PART, int... N>
+  __device__ __forceinline__ void reads_at(std::integer_sequence<int, N...>, Frags &f) {
+    (read_if<H, J, M, PART, N>(f), ...);
+  }
+
+  // Loads at period position P of half H of round p.
+  template <int H, int P, int I>
+  __device__ __forceinline__ void load_if(int p) {
+    if constexpr (P >= kPos2 && (P - kPos2) % kLS == 0 && (P - kPos2) / kLS == I) load6<H % 2, I>(6 * p + 3 * H + 2);
+    if constexpr (P >= kPos3 && (P - kPos3) % kLS == 0 && (P - kPos3) / kLS == I) load6<(H + 1) % 2, I>(6 * p + 3 * H + 3);
+    if constexpr (P >= kPos4 && (P - kPos4) % kLS == 0 && (P - kPos4) / kLS == I) load6<H % 2, I>(6 * p + 3 * H + 4);
+    // The end of the previous period's ell 4 (this period's ell 1).
+    if constexpr (P + 128 >= kPos4 && (P + 128 - kPos4) % kLS == 0 && (P + 128 - kPos4) / kLS == I)
+      load6<(H + 1) % 2, I>(6 * p + 3 * H + 1);
+  }
+  template <int H, int P, int... I>
+  __device__ __forceinline__ void loads_at(std::integer_sequence<int, I...>, int p) {
+    (load_if<H, P, I>(p), ...);
+  }
+
+  // The 4 scale bytes per row of step pair U (0..7) of a round: dwords U and
+  // U + 1 of chunk 2 p (sc_ck) and chunk 2 p + 1 (sc_ckn), shifted by the
+  // row's byte offset; pair 7 shifts in the first dword of chunk 2 p + 2,
+  // which replaced chunk 2 p in sc_ck by then.  The MFMA of step 2 u + s in
+  // half-wave w uses group 2 s + w, so lanes 0-31 take groups 0, 2 and
+  // lanes 32-63 groups 1, 3, in byte s.  t: the pair's index over all of K.
+  template <int U>
+  __device__ __forceinline__ void convert6(int t) {
+    const uint32_t keep = keep_mask(a.kb - 4 * t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w0 = U < 4 ? sc_ck[j][U] : sc_ckn[j][U - 4];
+      const uint32_t w1 = U == 3 ? sc_ckn[j][0] : U == 7 ? sc_ck[j][0] : U < 4 ? sc_ck[j][U + 1] : sc_ckn[j][U - 3];
+      const uint32_t d = __builtin_amdgcn_alignbyte(w1, w0, sc_sh[j]) & keep;
+      const uint32_t lo = __builtin_amdgcn_perm(0u, d, 0x0c0c0200u);  // groups 0, 2
+      const uint32_t hi = __builtin_amdgcn_perm(0u, d, 0x0c0c0301u);  // groups 1, 3
+      const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+      sc_set[U & 1][2 * j] = (int)sw[0];
+      sc_set[U & 1][2 * j + 1] = (int)sw[1];
+    }
+  }
+
+  // MFMA M of step JJ (0..15) of round p.
+  template <int JJ, int M>
+  __device__ __forceinline__ void mstep6(int p, Frags &f0, Frags &f1) {
+    constexpr int H = JJ / 8, J = JJ % 8, P = 16 * J + M;
+    if constexpr (M == kMB && (J == 1 || J == 4 || J == 6 || J == 7)) {
+      if constexpr (J == 1 || J == 4)
+        wait_vm_lgkm0<0>();
+      else if constexpr (J == 6)
+        wait_vm_lgkm0<63>();
+      else
+        wait_vm_lgkm0<vm_at7()>();
+      barrier();
+      if constexpr (JJ == 6) fetch_chunk<0>(sc_ck);    // chunk 2 p + 2
+      if constexpr (JJ == 14) fetch_chunk<1>(sc_ckn);  // chunk 2 p + 3
+      if constexpr (JJ == 15) stage_group(p + 2);
+    }
+    if constexpr (M == 2 && (JJ & 1)) convert6<((JJ + 1) / 2) % 8>(8 * p + (JJ + 1) / 2);
+    Frags &fn = (JJ % 2 == 0) ? f1 : f0;  // the next step's fragments
+    if constexpr (J == 1 || J == 4) {
+      if constexpr (M < kMB)
+        reads_at<H, J, M, 0>(std::make_integer_sequence<int, n_reads(J, 0)>(), fn);
+      else
+        reads_at<H, J, M, 1>(std::make_integer_sequence<int, n_reads(J, 1)>(), fn);
+    } else {
+      reads_at<H, J, M, 0>(std::make_integer_sequence<int, n_reads(J, 0)>(), fn);
+    }
+    loads_at<H, P>(std::make_integer_sequence<int, 2 * kL6>(), p);
+    // x blocks in order, y blocks snaking (as in the other kinds).
+    constexpr int I = M / 4, J0 = M % 4, Y = (I & 1) ? 3 - J0 : J0;
+    const Frags &f = (JJ % 2 == 0) ? f0 : f1;
+    acc[I][Y] = mma<false, JJ & 1>(f.x[I], f.y[Y], acc[I][Y], sc_set[(JJ / 2) & 1][I], sc_set[(JJ / 2) & 1][4 + Y]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int JJ, int... M>
+  __device__ __forceinline__ void kstep6(std::integer_sequence<int, M...>, int p, Frags &f0, Frags &f1) {
+    (mstep6<JJ, M>(p, f0, f1), ...);
+  }
+  template <int... JJ>
+  __device__ __forceinline__ void round6(std::integer_sequence<int, JJ...>, int p, Frags &f0, Frags &f1) {
+    (kstep6<JJ>(std::make_integer_sequence<int, 16>(), p, f0, f1), ...);
+  }
+  // The steps k0 + JJ < nks of a last, partial round.
+  template <int... JJ>
+  __device__ __forceinline__ void tail6(std::integer_sequence<int, JJ...>, int p, int left, Frags &f0, Frags &f1) {
+    ((JJ < left ? kstep6<JJ>(std::make_integer_sequence<int, 16>(), p, f0, f1) : void()), ...);
+  }
+
+  __device__ __forceinline__ void run6() {
+    static_assert(TM == 256 && TN == 256 && kNBn == 4 && kNBm == 4, "fp6: 256 x 256 tiles, 32 x 32 blocks");
+    // Panels: rows a.lda (= a.ldb) bytes apart; the resource ends with the
+    // last valid row.
+    const int ld = a.lda;
+    rs6[0] = make_rsrc(a.A + (size_t)m0 * ld, (uint32_t)min(a.M - m0, TM) * (uint32_t)ld);
+    rs6[1] = make_rsrc(a.B + (size_t)n0 * ld, (uint32_t)min(a.N - n0, TN) * (uint32_t)ld);
+    // Piece n = 64 (kL6 w + i) + l of a slot (144-byte rows of 9 pieces):
+    // row n / 9, piece n % 9 (the ninth is unused and loads nothing).
+#pragma unroll
+    for (int i = 0; i < kL6; ++i) {
+      const int n = 64 * (kL6 * wave + i) + lane, r = n / 9, c = n - 9 * r;
+      l6off[i] = c < 8 ? (uint32_t)r * (uint32_t)ld + 16u * (uint32_t)c : kOOB;
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int h24 = 24 * (lane >> 5);
+      rbh[sl][0] = slots.a[sl] + (wave_m * kWM + (lane & 31)) * T::kPitch;
+      rbh[sl][1] = slots.b[sl] + (wave_n * kWN + (lane & 31)) * T::kPitch;
+      rb[sl][0] = rbh[sl][0] + h24;
+      rb[sl][1] = rbh[sl][1] + h24;
+    }
+    const int nks = a.ksteps;  // K steps of 64 elements
+
+    // Prologue: group 0 of the scales, line 0 into slot 0, and the loads of
+    // line 1 that the K loop's previous period would have issued (the rest
+    // go out in steps 0 and 1).
+    stage_group(0);
+    load_line6_first<0>(0, std::make_integer_sequence<int, 2 * kL6>());
+    constexpr int kEarly1 = (128 - kPos4 + kLS - 1) / kLS;  // ell 4 loads issued in its own period
+    load_line6_first<1>(1, std::make_integer_sequence<int, kEarly1>());
+    wait_vm_lgkm0<kEarly1>();
+    barrier();
+    fetch_chunk<0>(sc_ck);
+    fetch_chunk<1>(sc_ckn);
+    convert6<0>(0);
+    Frags f0, f1;
+    read_first6(std::make_integer_sequence<int, 24>(), f0);
+    // Every wave has read group 0 before group 1 replaces it.
+    wait_vm_lgkm0<kEarly1>();
+    barrier();
+    stage_group(1);
+
+    int k = 0, p = 0;
+    for (; k + 16 <= nks; k += 16, ++p) round6(std::make_integer_sequence<int, 16>(), p, f0, f1);
+    if (k < nks) tail6(std::make_integer_sequence<int, 16>(), p, nks - k, f0, f1);
+    wait_vm_lgkm0<0>();
+    fence_acc();
+    epilogue();
+  }
+  template <int S, int... I>
+  __device__ __forceinline__ void load_line6_first(int L, std::integer_sequence<int, I...>) {
+    (load6<S, I>(L), ...);
+  }
+  // Step 0's fragments (line 0, slot 0).
+  template <int... N>
+  __device__ __forceinline__ void read_first6(std::integer_sequence<int, N...>, Frags &f) {
+    (piece6<0, kFragOrder[N / 3], N % 3, 0, 8 * (N % 3)>(f), ...);
   }
 
   // K split: the tile's fp32 sums into plane `split` of the workspace (M x N,
@@ -1355,12 +1536,6 @@ void gemm_kernel(const Args a) {
   slots.a[1] = (LDS_AS uint8_t *)sA1;
   slots.b[0] = (LDS_AS uint8_t *)sB0;
   slots.b[1] = (LDS_AS uint8_t *)sB1;
-  if constexpr (kSlots<T, TM, TN> == 3) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sA2[TM * T::kPitch];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB2[TN * T::kPitch];
-    slots.a[2] = (LDS_AS uint8_t *)sA2;
-    slots.b[2] = (LDS_AS uint8_t *)sB2;
-  }
   if constexpr (kSlots<T, TM, TN> == 4) {
     __shared__ __attribute__((aligned(1024))) uint8_t sA2[TM * kRowBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t sA3[TM * kRowBytes];
@@ -1606,9 +1781,10 @@ hipError_t launch(const Problem &p) {
   }
   const bool fp6 = p.dt == Dt::kMxfp6E2M3 || p.dt == Dt::kMxfp6E3M2;
   if (fp6) {
-    // Rows of bytes (four elements in three), 96-byte slices, a scale per 32.
+    // Rows of bytes (four elements in three), a scale per 32; the K loop
+    // counts 64-element steps (48 bytes; K % 64 == 0).
     a.K = (int)(p.K / 4 * 3);
-    a.ksteps = (a.K + 95) / 96;
+    a.ksteps = (int)(p.K / 64);
     a.kb = (int)((p.K + 31) / 32);
   }
   const bool scaled = p.dt == Dt::kMxfp8 || p.dt == Dt::kMxfp4 || fp6;
