@@ -1158,6 +1158,7 @@ struct Kernel {
   __amdgpu_buffer_rsrc_t rs6[2];   // the A and B panels of the tile
   const LDS_AS uint8_t *rb[2][2];  // [slot][0: A, 1: B]: this lane's fragment row (block 0) + 24 (lane / 32)
   const LDS_AS uint8_t *rbh[2][2]; // the same without the half-wave's 24 bytes
+  u32x2 t6[8][3];                  // MODE 2 pieces between their read and their merge
 
   // Load instruction I (A: 0 .. kL6 - 1, B: kL6 ..) of line L into slot S.
   // Past the last row the range check returns zeros; past a row's end the
@@ -1180,24 +1181,31 @@ struct Kernel {
     constexpr int off = (R % 4) * 32 * T::kPitch + X;
     static_assert(X >= 0 && off < 65536, "constant LDS offset");
     if constexpr (R < kNBn)
-      piece6_into<S, op, Q, MODE, off>(f.x[R]);
+      piece6_into<S, op, Q, MODE, off, R>(f.x[R]);
     else
-      piece6_into<S, op, Q, MODE, off>(f.y[R - kNBn]);
+      piece6_into<S, op, Q, MODE, off, R>(f.y[R - kNBn]);
   }
   // (MODE 1 reads for every lane, from rbh: the upper half-wave takes bytes
-  // of its own row that its MODE 2 read replaces.  MODE 2 merges with a
-  // select: a branch around the read made the compiler spill.)
-  template <int S, int OP, int Q, int MODE, int OFF>
+  // of its own row that its MODE 2 read replaces.  A MODE 2 read lands in
+  // t6 and is merged into the fragment with a select kMD MFMAs later
+  // (merge6): a select right after the read waited for it in the middle of
+  // the MFMA stream, and a branch around the read made the compiler spill.)
+  template <int S, int OP, int Q, int MODE, int OFF, int R>
   __device__ __forceinline__ void piece6_into(Frag &fr) {
     const u32x2 v = *(const LDS_AS u32x2 *)((MODE == 0 ? rb[S][OP] : rbh[S][OP]) + OFF);
     if constexpr (MODE < 2) {
       fr[2 * Q] = (int)v[0];
       fr[2 * Q + 1] = (int)v[1];
     } else {
-      const bool up = lane >= 32;
-      fr[2 * Q] = up ? (int)v[0] : fr[2 * Q];
-      fr[2 * Q + 1] = up ? (int)v[1] : fr[2 * Q + 1];
+      t6[R][Q] = v;
     }
+  }
+  template <int R, int Q>
+  __device__ __forceinline__ void merge6(Frags &f) {
+    Frag &fr = R < kNBn ? f.x[R % kNBn] : f.y[R % kNBm];
+    const bool up = lane >= 32;
+    fr[2 * Q] = up ? (int)t6[R][Q][0] : fr[2 * Q];
+    fr[2 * Q + 1] = up ? (int)t6[R][Q][1] : fr[2 * Q + 1];
   }
 
   // The reads of step J's successor, in the order y0, x0, y1, y2, y3, x1,
@@ -1238,6 +1246,25 @@ struct Kernel {
   }
   static constexpr int rd_m(int J, int part, int n) {
     return rd_m0(J, part) + n * (rd_m1(J, part) - rd_m0(J, part)) / n_reads(J, part);
+  }
+
+  // Merge of MODE 2 read n of step J (1 or 4): kMD MFMAs after the read,
+  // as a position counted from the start of step J (16 and on: the next
+  // step, which first takes fragment x i at its MFMA 4 i, y j at MFMA j).
+  static constexpr int kMD = 3;
+  static constexpr int merge_pos(int J, int n) {
+    const Rd d = read_of(J, 1, n);
+    const int want = rd_m(J, 1, n) + kMD;
+    const int use = 16 + (d.r < 4 ? 4 * d.r : 0);
+    return want < use ? want : use;
+  }
+  template <int J, int POS, int N>
+  __device__ __forceinline__ void merge_if(Frags &f) {
+    if constexpr (read_of(J, 1, N).mode == 2 && merge_pos(J, N) == POS) merge6<read_of(J, 1, N).r, read_of(J, 1, N).q>(f);
+  }
+  template <int J, int POS, int... N>
+  __device__ __forceinline__ void merges_at(std::integer_sequence<int, N...>, Frags &f) {
+    (merge_if<J, POS, N>(f), ...);
   }
 
   template <int H, int J, int M, int PART, int N>
@@ -1307,14 +1334,18 @@ struct Kernel {
     }
     if constexpr (M == 2 && (JJ & 1)) convert6<((JJ + 1) / 2) % 8>(8 * p + (JJ + 1) / 2);
     Frags &fn = (JJ % 2 == 0) ? f1 : f0;  // the next step's fragments
+    Frags &fc = (JJ % 2 == 0) ? f0 : f1;  // this step's
     if constexpr (J == 1 || J == 4) {
       if constexpr (M < kMB)
         reads_at<H, J, M, 0>(std::make_integer_sequence<int, n_reads(J, 0)>(), fn);
       else
         reads_at<H, J, M, 1>(std::make_integer_sequence<int, n_reads(J, 1)>(), fn);
+      merges_at<J, M>(std::make_integer_sequence<int, n_reads(J, 1)>(), fn);
     } else {
       reads_at<H, J, M, 0>(std::make_integer_sequence<int, n_reads(J, 0)>(), fn);
     }
+    // Merges of the previous step's MODE 2 reads that fall in this step.
+    if constexpr (J == 2 || J == 5) merges_at<J - 1, 16 + M>(std::make_integer_sequence<int, n_reads(J - 1, 1)>(), fc);
     loads_at<H, P>(std::make_integer_sequence<int, 2 * kL6>(), p);
     // x blocks in order, y blocks snaking (as in the other kinds).
     constexpr int I = M / 4, J0 = M % 4, Y = (I & 1) ? 3 - J0 : J0;
