@@ -118,7 +118,7 @@ struct Traits {
   static constexpr bool kFp6 = DT == kFp6E2M3 || DT == kFp6E3M2;
   static constexpr int kElem = kScaled ? 1 : 2;
   static constexpr int kSliceBytes = 128;                  // global bytes of a row per K slice (fp6: line stage)
-  static constexpr int kPitch = kFp6 ? 144 : kSliceBytes;  // LDS bytes of a slot row
+  static constexpr int kPitch = kSliceBytes;               // LDS bytes of a slot row
   static constexpr bool kAK = AK, kBK = BK;
 };
 
@@ -330,7 +330,7 @@ struct MNLoader {
 // The kernel.
 // ---------------------------------------------------------------------------
 // LDS slots of the K-slice ring.  The 256-row tiles fill the LDS with two
-// (2 x 64 KiB; fp6: 2 x 72 KiB of 144-byte rows).  A 128 x 128 tile's slice holds a quarter of the MFMA work
+// (2 x 64 KiB).  A 128 x 128 tile's slice holds a quarter of the MFMA work
 // of a 256 x 256 one, too little to cover the latency of the next slice's
 // loads with one slice in flight, so its ring has four slots (4 x 32 KiB):
 // the loads of slice kt + 4 go out in slice kt, three slices ahead of use.
@@ -1103,10 +1103,15 @@ struct Kernel {
   // two lines: 1.5 lines per row per 96 bytes.  Here the loads stage whole
   // lines instead, stage L being row bytes 128 L .. 128 L + 127 of every
   // row of the tile, so every byte crosses from L2 once: three stages per
-  // period of 8 K steps (384 bytes).  Two slots hold two stages; a slot row
-  // is 144 bytes (the line and 16 unused bytes), so that the 32 rows a
-  // fragment read takes meet at most two to a bank pair and every read
-  // address is a per-lane base plus a constant.
+  // period of 8 K steps (384 bytes).  Two slots hold two stages, in rows of
+  // 128 bytes with the 16-byte chunks permuted as in the other kinds' slots
+  // (the 32 rows of a fragment read, 8 bytes each at one line byte, meet at
+  // most two to a bank pair, the least 8-byte reads of 16-byte aligned rows
+  // allow).  A slot row of 144 bytes instead (the line and an unused piece,
+  // so that every read address was a per-lane base plus a constant) cost
+  // one load lane in nine and measured 4% slower; rows shifted so the reads
+  // met no bank conflict loaded 8 bytes of the neighbouring lines and
+  // measured 15% slower: these loads, not the LDS, bound this kernel.
   //
   // Inside a period, step J (0..7) takes bytes 48 J .. 48 J + 47 of its
   // period: steps 0, 1 lie in the period's first line (ell 0), 3, 4 in the
@@ -1134,7 +1139,7 @@ struct Kernel {
   // group p + 1.  Pair u (steps 2 u, 2 u + 1) of a round has its 4 bytes
   // converted in step 2 u - 1 into set u % 2.
   // -------------------------------------------------------------------------
-  static constexpr int kL6 = 9;   // load instructions per wave per operand and line (256 rows x 9 16-byte pieces / 4 waves / 64)
+  static constexpr int kL6 = 8;   // load instructions per wave per operand and line
   static constexpr int kMB = 8;   // MFMA of a step at which its barrier goes
   static constexpr int kLS = 2;   // MFMAs between two load instructions of a line
   // Period position (16 J + MFMA) of load instruction i of the lines issued
@@ -1154,10 +1159,10 @@ struct Kernel {
     return n;
   }
 
-  uint32_t l6off[kL6];             // per instruction: byte offset of this lane's piece in the panel, or kOOB
-  __amdgpu_buffer_rsrc_t rs6[2];   // the A and B panels of the tile
-  const LDS_AS uint8_t *rb[2][2];  // [slot][0: A, 1: B]: this lane's fragment row (block 0) + 24 (lane / 32)
-  const LDS_AS uint8_t *rbh[2][2]; // the same without the half-wave's 24 bytes
+  uint32_t l6off[2];                 // this lane's piece in even / odd load instructions (panel byte offset)
+  __amdgpu_buffer_rsrc_t rs6[2];     // the A and B panels of the tile
+  const LDS_AS uint8_t *rowb[2][2];  // [slot][0: A, 1: B]: this lane's fragment row (block 0)
+  uint32_t swz16, a24;               // the row's chunk permutation (x 16); 24 (lane / 32)
   u32x2 t6[8][3];                  // MODE 2 pieces between their read and their merge
 
   // Load instruction I (A: 0 .. kL6 - 1, B: kL6 ..) of line L into slot S.
@@ -1167,7 +1172,9 @@ struct Kernel {
   __device__ __forceinline__ void load6(int L) {
     constexpr int op = I < kL6 ? 0 : 1, i = I % kL6;
     LDS_AS uint8_t *dst = (op ? slots.b[S] : slots.a[S]) + (kL6 * wave + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs6[op], (LDS_AS void *)dst, 16, l6off[i], (uint32_t)(128 * L), 0, 0);
+    // (Instruction i takes rows 8 i further: by soffset.)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs6[op], (LDS_AS void *)dst, 16, l6off[i & 1],
+                                             (uint32_t)(128 * L + 8 * i * a.lda), 0, 0);
   }
 
   // Piece Q (bytes 8 Q .. 8 Q + 7, registers 2 Q and 2 Q + 1) of fragment R
@@ -1178,21 +1185,23 @@ struct Kernel {
   template <int S, int R, int Q, int MODE, int X>
   __device__ __forceinline__ void piece6(Frags &f) {
     constexpr int op = R < kNBn ? 1 : 0;
-    constexpr int off = (R % 4) * 32 * T::kPitch + X;
-    static_assert(X >= 0 && off < 65536, "constant LDS offset");
+    static_assert(X >= 0 && (R % 4) * 32 * T::kPitch + X < 65536, "constant LDS offset");
     if constexpr (R < kNBn)
-      piece6_into<S, op, Q, MODE, off, R>(f.x[R]);
+      piece6_into<S, op, Q, MODE, X, R>(f.x[R]);
     else
-      piece6_into<S, op, Q, MODE, off, R>(f.y[R - kNBn]);
+      piece6_into<S, op, Q, MODE, X, R>(f.y[R - kNBn]);
   }
-  // (MODE 1 reads for every lane, from rbh: the upper half-wave takes bytes
+  // (MODE 1 reads for every lane at byte X: the upper half-wave takes bytes
   // of its own row that its MODE 2 read replaces.  A MODE 2 read lands in
   // t6 and is merged into the fragment with a select kMD MFMAs later
   // (merge6): a select right after the read waited for it in the middle of
   // the MFMA stream, and a branch around the read made the compiler spill.)
-  template <int S, int OP, int Q, int MODE, int OFF, int R>
+  template <int S, int OP, int Q, int MODE, int X, int R>
   __device__ __forceinline__ void piece6_into(Frag &fr) {
-    const u32x2 v = *(const LDS_AS u32x2 *)((MODE == 0 ? rb[S][OP] : rbh[S][OP]) + OFF);
+    // Line byte x of the row at its permuted chunk: x ^ swz16 (x & 15 is 0
+    // or 8, so the permutation keeps the 8-byte half).
+    const LDS_AS uint8_t *p = rowb[S][OP] + (((uint32_t)X + (MODE == 0 ? a24 : 0u)) ^ swz16) + (R % 4) * 32 * 128;
+    const u32x2 v = *(const LDS_AS u32x2 *)p;
     if constexpr (MODE < 2) {
       fr[2 * Q] = (int)v[0];
       fr[2 * Q + 1] = (int)v[1];
@@ -1355,6 +1364,10 @@ struct Kernel {
   }
   template <int JJ, int... M>
   __device__ __forceinline__ void kstep6(std::integer_sequence<int, M...>, int p, Frags &f0, Frags &f1) {
+    // (The read addresses are per-lane constants; without this the compiler
+    // computes them all ahead of the loop and holds them in registers, which
+    // made it spill.)
+    asm volatile("" : "+v"(swz16), "+v"(a24));
     (mstep6<JJ, M>(p, f0, f1), ...);
   }
   template <int... JJ>
@@ -1374,20 +1387,21 @@ struct Kernel {
     const int ld = a.lda;
     rs6[0] = make_rsrc(a.A + (size_t)m0 * ld, (uint32_t)min(a.M - m0, TM) * (uint32_t)ld);
     rs6[1] = make_rsrc(a.B + (size_t)n0 * ld, (uint32_t)min(a.N - n0, TN) * (uint32_t)ld);
-    // Piece n = 64 (kL6 w + i) + l of a slot (144-byte rows of 9 pieces):
-    // row n / 9, piece n % 9 (the ninth is unused and loads nothing).
+    // Slot rows of 128 bytes with the 16-byte chunks permuted as in the
+    // other kinds' slots: lane l of load instruction i of wave w writes row
+    // 64 w + 8 i + l / 8, physical chunk l % 8, holding logical chunk
+    // (l % 8) ^ swz(row); swz depends on i only through its parity.
 #pragma unroll
-    for (int i = 0; i < kL6; ++i) {
-      const int n = 64 * (kL6 * wave + i) + lane, r = n / 9, c = n - 9 * r;
-      l6off[i] = c < 8 ? (uint32_t)r * (uint32_t)ld + 16u * (uint32_t)c : kOOB;
+    for (int i = 0; i < 2; ++i) {
+      const int r = 64 * wave + 8 * i + (lane >> 3), c = (lane & 7) ^ swz(r);
+      l6off[i] = (uint32_t)(64 * wave + (lane >> 3)) * (uint32_t)ld + 16u * (uint32_t)c;
     }
+    swz16 = (uint32_t)swz(lane & 31) << 4;  // fragment rows start at multiples of 32
+    a24 = 24u * (uint32_t)(lane >> 5);
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
-      const int h24 = 24 * (lane >> 5);
-      rbh[sl][0] = slots.a[sl] + (wave_m * kWM + (lane & 31)) * T::kPitch;
-      rbh[sl][1] = slots.b[sl] + (wave_n * kWN + (lane & 31)) * T::kPitch;
-      rb[sl][0] = rbh[sl][0] + h24;
-      rb[sl][1] = rbh[sl][1] + h24;
+      rowb[sl][0] = slots.a[sl] + (wave_m * kWM + (lane & 31)) * 128;
+      rowb[sl][1] = slots.b[sl] + (wave_n * kWN + (lane & 31)) * 128;
     }
     const int nks = a.ksteps;  // K steps of 64 elements
 
