@@ -5,8 +5,9 @@
 // that fills the chip better -- and each wave a TM/2 x TN/2 sub-tile of fp32
 // accumulators (in AGPRs; 256 per lane for 256 x 256).  The K loop walks
 // slices of the A and B panels (128 bytes of a row: 64 bf16/fp16, 128 fp8
-// or 256 fp4 elements; 96 bytes, 128 elements, for fp6) through a ring of
-// LDS slots per operand.
+// or 256 fp4 elements) through a ring of LDS slots per operand; fp6 runs
+// 64-element K steps (48 bytes) over whole 128-byte lines of its rows (the
+// fp6 section below).
 //
 // Where this follows the pages and where it departs:
 //  * tile grid: ceil-div over N and M as in the TileLang SM100 README
@@ -24,18 +25,19 @@
 //    Out-of-range rows take an out-of-range buffer offset and arrive as
 //    zeros (the pages' TMA zero OOB fill).  The ragged last K slice of a
 //    K-contiguous operand is zeroed in LDS past column K once it has landed
-//    (MXFP8 with a ragged K, MXFP4 with a ragged K and MXFP6 check columns
-//    in their loads instead); a K-major operand's rows past K read as zeros.
+//    (MXFP8 and MXFP4 with a ragged K check columns in their loads instead;
+//    MXFP6 never reads past a row's last K step); a K-major operand's rows
+//    past K read as zeros.
 //  * pipelined K loop: the pages use a 3-slot ring with producer and
 //    consumer warpgroups and mbarrier parity waits (velog "tilelang",
 //    Device IRModule).  Here every wave both loads and computes, with a
-//    ring of NS slots (two for 256-row tiles, three for fp6, four for
-//    128 x 128 and 64 x 64): partway through slice kt's MFMAs (halfway, or
-//    three quarters for fp8) a wait and a barrier free slot kt % NS; the
-//    loads of slice kt + NS into it then go out spread over the next half
-//    slice of MFMAs (three quarters for fp4 and fp6).  The next slice's
-//    first operand reads follow the barrier, overlapping the current
-//    slice's remaining MFMAs.
+//    ring of NS slots (two for 256-row tiles, four for 128 x 128 and
+//    64 x 64): partway through slice kt's MFMAs (halfway, or three quarters
+//    for fp8) a wait and a barrier free slot kt % NS; the loads of slice
+//    kt + NS into it then go out spread over the next half slice of MFMAs
+//    (three quarters for fp4).  The next slice's first operand reads follow
+//    the barrier, overlapping the current slice's remaining MFMAs.  fp6:
+//    two slots of line stages, four barriers per 8 K steps.
 //  * wave-tile MMA: v_mfma_f32_16x16x32_{bf16,f16} (8 x 8 blocks per wave)
 //    and, for the block-scaled kinds, v_mfma_scale_f32_32x32x64_f8f6f4
 //    (4 x 4 blocks) with the e8m0 block scales as operands (TCGEN05
@@ -721,7 +723,8 @@ struct Kernel {
   // Zero the chunks of the ragged last slice kt (in slot S) past column K,
   // after this wave's loads of it have landed and before the barrier that
   // lets the workgroup read it.  (K-major operands need nothing: their rows
-  // past K read as zeros.  MXFP8 and MXFP6 check columns in their loads.)
+  // past K read as zeros.  MXFP8 and MXFP4 with a ragged K check columns in
+  // their loads; MXFP6 reads no byte past a row's last K step.)
   static constexpr bool kZeroTail = !T::kScaled && (T::kAK || T::kBK);
   template <int S>
   __device__ __forceinline__ void zero_tail(int kt) {
