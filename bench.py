@@ -41,6 +41,13 @@ written, which evicts the inputs from the L2s and the 256 MB Infinity
 Cache; each region is followed by the same region of flushes alone, whose
 time is subtracted.
 
+--zero-elements is a clock diagnostic: the same launches on inputs whose
+elements are all zero (block scales kept).  The kernels run the same
+instructions and cycles, but without data-dependent switching the board
+stays below its power limit; the clock it then holds, against the one on
+the workload's data, shows how much of the time the power limit sets.  Its
+line says so under "data" and is not a measurement of the workload.
+
 The line also carries:
   roofline     `traffic` is the HBM bytes per launch from rocprofv3
                FETCH_SIZE/WRITE_SIZE counters, calibrated on a plain copy,
@@ -537,6 +544,9 @@ def main():
                     help="16-bit workloads: call the K-split entry point with S splits (0: the library "
                          "chooses); default: the plain entry point")
     ap.add_argument("--record-traffic", metavar="DIR")
+    ap.add_argument("--zero-elements", action="store_true",
+                    help="clock diagnostic: A's and B's elements all zero (block scales kept), so the same "
+                         "instruction stream runs without data-dependent switching; not the workload's data")
     args = ap.parse_args()
 
     if args.record_traffic:
@@ -573,6 +583,12 @@ def main():
         tg.set_tile(*tile)
     log(f"[bench] {w.description}: generating inputs")
     x, dev = device_inputs(w)
+    if args.zero_elements:
+        import numpy as np
+        for k in ("A", "B", "qA", "qB"):
+            if k in x:
+                x[k] = np.zeros_like(x[k])
+                dev[k].zero_()
     out_dtype = torch.float16 if w.kind == "f16_nn" else torch.bfloat16
     out = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
     stream = torch.cuda.Stream()
@@ -689,7 +705,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f16": "f16", "mxfp8": "fp8e4m3+e8m0", "mxfp4": "fp4e2m1+e8m0",
                   "mxfp6": f"fp6{workloads.fp6_format(w.kind) if prec == 'mxfp6' else ''}+e8m0"}[prec],
-        "data": "synthetic",
+        "data": "synthetic, A and B elements all zero (clock diagnostic)" if args.zero_elements else "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "layout": "NT" if w.kind != "f16_nn" else "NN",
                    "accumulate": "fp32",
