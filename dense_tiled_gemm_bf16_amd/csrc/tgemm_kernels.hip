@@ -112,9 +112,12 @@ enum : int { kBf16 = 0, kF16 = 1, kFp8 = 2, kFp4 = 3, kFp6E2M3 = 4, kFp6E3M2 = 5
 template <int DT, bool AK, bool BK, bool WHOLE = false>
 struct Traits {
   static constexpr int kDt = DT;
-  // MXFP8 with K a positive multiple of the slice: no slice is ragged, so
-  // its loads check no columns (otherwise they do, as MXFP6's always do; the
-  // other kinds never do, and zero the ragged slice's tail in LDS instead).
+  // MXFP8 and MXFP4 with K a positive multiple of the slice: no slice is
+  // ragged, so their loads check no columns (otherwise they do, as MXFP6's
+  // always do; the other kinds never do, and zero the ragged slice's tail in
+  // LDS instead).  For MXFP4 it also means dword-aligned scale rows (both
+  // scale arrays dword-aligned; K a multiple of 256 makes every row's 8 K/256
+  // scale bytes a whole number of dwords).
   static constexpr bool kWholeK = WHOLE;
   static constexpr bool kScaled = DT >= kFp8;
   static constexpr bool kFp6 = DT == kFp6E2M3 || DT == kFp6E3M2;
@@ -359,16 +362,18 @@ struct Kernel {
   // MFMA shape.  16-bit inputs: v_mfma_f32_16x16x32 (it reads and writes 4
   // accumulators per 16 K flops, half the accumulator traffic per flop of
   // the 32 x 32 x 16 form; under full load the chip is power-capped, and the
-  // lower-energy form runs at a higher clock).  fp8: the scaled 32 x 32 x 64
-  // form.  Either way a slice is two K substeps.
-  static constexpr bool kW = T::kScaled;        // 32 x 32 blocks
+  // lower-energy form runs at a higher clock).  fp4: the scaled 16 x 16 x 128
+  // form for the same reason (in a register-only stream of random operands
+  // under the power limit it delivered 13% more flops per second than the
+  // 32 x 32 x 64 form); its 16-byte fragments are laid out like the 16-bit
+  // kinds'.  fp8: the scaled 32 x 32 x 64 form.  Either way a slice is two K
+  // substeps.
+  static constexpr bool kW = T::kScaled && T::kDt != kFp4;  // 32 x 32 blocks
   static constexpr int kBlk = kW ? 32 : 16;
   static constexpr int kNBm = kWM / kBlk;       // blocks per wave along M (y blocks)
   static constexpr int kNBn = kWN / kBlk;       // blocks per wave along N (x blocks)
   static constexpr int kNR = kNBm + kNBn;       // fragment reads per substep
-  // fp4: a 32-byte fragment holds 64 K elements, two MFMAs of 32 per lane.
-  static constexpr int kHalves = T::kDt == kFp4 ? 2 : 1;
-  static constexpr int kPerSub = kNBm * kNBn * kHalves;  // MFMAs per substep
+  static constexpr int kPerSub = kNBm * kNBn;   // MFMAs per substep
   static constexpr int kMfma = 2 * kPerSub;     // MFMAs per slice
   // Load instructions per wave per slice: 8 rows of 128 bytes each (fp6 has
   // its own K loop, below).
@@ -412,7 +417,7 @@ struct Kernel {
   static constexpr bool kPfHead = kLastLoad >= kMfma;  // last load in the next slice's head
   static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
   // (Not for fp6, which has its own K loop.)
-  static constexpr int kPfDist = T::kScaled && !T::kFp6 ? 3 : 0;
+  static constexpr int kPfDist = T::kScaled && !T::kFp6 && !(T::kDt == kFp4 && T::kWholeK) ? 3 : 0;
   static_assert(kPfDist == 0 || !kPfHead || kPfAt < kBarrierAt, "prefetch goes before the barrier it may pass");
   static_assert(kPfDist == 0 || kPfHead || kPfAt < kMfma, "prefetch position");
   static_assert(kPfDist == 0 || kFreeAt == kBarrierAt, "the prefetch placement assumes one barrier per slice");
@@ -482,30 +487,58 @@ struct Kernel {
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
   u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction (fp6: chunks 2 p and 2 p + 1 of round p)
   // fp4, fp6: the scale chunks of every row of the tile are loaded into LDS
-  // once per workgroup, two consecutive chunks of a row at a time (a
-  // "group": chunks 2 g and 2 g + 1; waves 0-1 the B rows, waves 2-3 the A
-  // rows), and each wave then reads the rows its MFMAs take (every row feeds
-  // two waves).  A load instruction takes 32 rows, lanes l and l + 32 the two
-  // chunks of row l, so it touches 32 cache lines for 1 KiB.  (Loading each
-  // wave's rows itself took 64 rows per instruction, one line per lane, and
-  // every row twice; one chunk of 64 rows per instruction, 64 lines, cost
-  // twice the line fetches of this for the same bytes.)  st_off: this lane's
-  // row and chunk in the wave's first load instruction (aligned byte offset,
-  // or kOOB); the other three are 32, 64 and 96 rows further, by soffset.
+  // once per workgroup (waves 0-1 the B rows, waves 2-3 the A rows), and
+  // each wave then reads the rows its MFMAs take (every row feeds two
+  // waves).
+  //  * fp6: two consecutive chunks of a row at a time (a "group": chunks
+  //    2 g and 2 g + 1).  A load instruction takes 32 rows, lanes l and
+  //    l + 32 the two chunks of row l, so it touches 32 cache lines for
+  //    1 KiB.  (Loading each wave's rows itself took 64 rows per
+  //    instruction, one line per lane, and every row twice.)  st_off: this
+  //    lane's row and chunk in the wave's first load instruction (aligned
+  //    byte offset, or kOOB); the other three are 32, 64 and 96 rows
+  //    further, by soffset.  Instruction i of wave w fills 1 KiB block
+  //    4 w + i: chunk q of row 32 i + r of the wave's 128 at bytes 512 q +
+  //    16 r.
+  //  * fp4 with dword-aligned scale rows: groups as for fp6, in two 16 KiB
+  //    slots (group g in slot g % 2); pair u of slices takes chunk u % 2 of
+  //    group u / 2.
+  //  * other fp4: one chunk at a time into a ring of three 8 KiB slots (chunk c
+  //    in slot c % 3), row R of the tile (B rows 0-255, then A rows) at
+  //    bytes 16 R of its slot; wave w's two load instructions take rows
+  //    128 w + 64 i + l.  A pair of slices reads chunks u and u + 1 (a
+  //    row's 16 scale bytes of the pair start inside chunk u when the row
+  //    does not start on a dword).  st_off: this lane's row in the first
+  //    instruction (aligned byte offset, or kOOB).
   static constexpr bool kStaged = T::kDt == kFp4 || T::kFp6;
-  // Bytes of the staging buffer: two 16-byte chunks of each of the tile's
-  // 256 B rows and 256 A rows.  Instruction i of wave w fills 1 KiB block
-  // 4 w + i: chunk q of row 32 i + r of the wave's 128 at bytes 512 q + 16 r.
-  static constexpr int kStageBytes = 512 * 32;
+  // fp4 with dword-aligned scale rows: two slots of groups (as fp6 stages
+  // them), pair u in chunk u % 2 of group u / 2.  (The L2 prefetch area goes
+  // to make room: 128 + 32 KiB fill the LDS.)
+  static constexpr bool kA4 = T::kDt == kFp4 && T::kWholeK;
+  static constexpr int kStageBytes = kA4 ? 2 * 512 * 32 : T::kDt == kFp4 ? 3 * 512 * 16 : 512 * 32;
   static constexpr int kChunkStride = 16;  // row bytes between consecutive chunks
   uint32_t st_off;
+  // fp4 (rows not dword-aligned): lane l = 16 g + r converts row r of
+  // blocks 4 g .. 4 g + 3 (x blocks 0-7, then y blocks 0-7): sh4, the byte
+  // shift of those rows inside a dword (16 rows apart, so the same for all
+  // four); rd4, the offset of the first in a chunk slot; the current pair's
+  // slot offsets (chunks u and u + 1) and the mask of the lane's bytes that
+  // hold scale blocks of the row.  Aligned rows: rd4, the offset of the
+  // first row in a group slot; sb4, the slot.
+  uint32_t sh4, rd4;
+  uint32_t keep4, cs4[2];
+  u32x4 t4[4];
+  uint32_t t4n[4];
+  uint32_t w4[4];  // one row's realigned dwords
+  u32x4 sv4[4];    // aligned rows: a group on its way from the L2 to its slot
+  const LDS_AS uint8_t *sb4;  // aligned rows: the slot of the pair being converted
   // Per block (4 x blocks, then 4 y blocks): fp8, the bytes of a group of 4
   // slices, converted into sc_nxt and copied into sc_cur before the group's
   // first slice.  fp4 and fp6 convert every slice's scales straight into
   // the set its MFMAs read (fp4: set kt % 2; fp6: set (k / 2) % 2 for K step
   // k), so no copy is needed at the start of a slice.
   int sc_nxt[8], sc_cur[8];
-  int sc_set[2][8];
+  int sc_set[2][kNR];
   Acc acc[kNBn][kNBm];
 
   __device__ __forceinline__ Kernel(const Args &args, const Slots &s) : a(args), slots(s) {}
@@ -526,9 +559,12 @@ struct Kernel {
       return r;
     } else {
       // 16 x 16 x 32: lane l holds row l % 16 and 8 elements of K: logical
-      // chunk 4 sub + l / 16.
+      // chunk 4 sub + l / 16.  fp4, 16 x 16 x 128: 32 elements (one K block
+      // of 16 bytes), chunk 2 (l / 16) + sub (the K block order of the fp4
+      // scales, below).
       const LDS_AS uint8_t *p = slot + (row0 + (lane & 15)) * kRowBytes;
-      return *(const LDS_AS u32x4 *)(p + (((4 * sub + (lane >> 4)) ^ lane_sw) << 4));
+      const int c = T::kDt == kFp4 ? 2 * (lane >> 4) + sub : 4 * sub + (lane >> 4);
+      return *(const LDS_AS u32x4 *)(p + ((c ^ lane_sw) << 4));
     }
   }
 
@@ -578,8 +614,8 @@ struct Kernel {
 
   // FIRST: the first K substep, whose MFMAs start from an accumulator of 0
   // (an inline constant), so the accumulators are never written by VALU code.
-  // SEL: byte of the scale registers to use; H: half of an fp4 fragment.
-  template <bool FIRST, int SEL = 0, int H = 0>
+  // SEL: byte of the scale registers to use.
+  template <bool FIRST, int SEL = 0>
   __device__ static __forceinline__ Acc mma(const Frag &x, const Frag &y, const Acc &c, int sx, int sy) {
     // The 16 x 16 forms are written as inline asm with the accumulator tied
     // in place ("+a"): with the builtin the register allocator rotates the
@@ -614,12 +650,33 @@ struct Kernel {
       const i32x8 y6 = {y[0], y[1], y[2], y[3], y[4], y[5], 0, 0};
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x6, y6, c, F, F, SEL, sx, SEL, sy);
     } else {
-      // Format code 4 (OCP FP4 E2M1): 16 bytes, 32 elements per lane, taken
-      // from half H of the fragment (the compiler reads the 4 registers in
-      // place); byte SEL of each scale VGPR.
-      const i32x8 xh = {x[4 * H], x[4 * H + 1], x[4 * H + 2], x[4 * H + 3], 0, 0, 0, 0};
-      const i32x8 yh = {y[4 * H], y[4 * H + 1], y[4 * H + 2], y[4 * H + 3], 0, 0, 0, 0};
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xh, yh, c, 4, 4, SEL, sx, SEL, sy);
+      // Format code 4 (OCP FP4 E2M1) for both operands (cbsz, blgp), 16 x 16
+      // x 128: 16 bytes, 32 elements per lane.  Byte SEL of each scale VGPR:
+      // op_sel bit 0 and op_sel_hi bit 1, the same for both.  Inline asm
+      // with the accumulator tied in place, as for the 16-bit forms.
+#define TGEMM_MFMA4(OPS) "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, " OPS " cbsz:4 blgp:4"
+      Acc d = c;
+      if constexpr (FIRST) {
+        if constexpr (SEL == 0)
+          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[0,0,0] op_sel_hi:[0,0,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 1)
+          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 2)
+          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[0,0,0] op_sel_hi:[1,1,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else
+          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[1,1,0] op_sel_hi:[1,1,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+      } else {
+        if constexpr (SEL == 0)
+          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[0,0,0] op_sel_hi:[0,0,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 1)
+          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 2)
+          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[0,0,0] op_sel_hi:[1,1,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else
+          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[1,1,0] op_sel_hi:[1,1,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+      }
+#undef TGEMM_MFMA4
+      return d;
     }
   }
 
@@ -754,8 +811,8 @@ struct Kernel {
 
   // fp4, fp6: group g (chunks 2 g and 2 g + 1) of this wave's 128 rows into
   // the staging buffer.
-  __device__ __forceinline__ void stage_group(int g) {
-    LDS_AS uint8_t *dst = slots.stage + wave * 4 * 1024;
+  __device__ __forceinline__ void stage_group(int g, int slot = 0) {
+    LDS_AS uint8_t *dst = slots.stage + slot * (512 * 32) + wave * 4 * 1024;
     // (A select on the wave-uniform operand, not rss[wave >> 1]: a dynamic
     // index into the member array would move the kernel's state to memory.)
     const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
@@ -782,43 +839,176 @@ struct Kernel {
     return nv >= 4 ? ~0u : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
   }
 
-  // fp4: slice t's 8 scale bytes per row, from chunk t / 2 (ODD: t odd, its
-  // second half, plus the next chunk's first dword), into sc_set[DST].  The
-  // two chunk buffers take turns: buffer CUR (0: sc_ck, 1: sc_ckn) holds
-  // chunk t / 2 and the other one the chunk after it.  Once an odd slice has
-  // been converted, chunk t / 2 is done with and chunk t / 2 + 2 is loaded
-  // into its buffer, so no register is ever copied to another: a copy at the
-  // loop's back edge waited for that load (18% of the cycles).
-  // The chunk after the next arrives from the staging buffer: at the odd
-  // slice t = 2 c + 1 (converted in slice 2 c), chunk c + 2, chunk PAR = c %
-  // 2 of the staged group, is read into the buffer chunk c leaves.  Group
-  // g + 2 is staged when slice 4 g + 4 is converted, in slice 4 g + 3: the
-  // last read of group g + 1 (chunk 2 g + 3, in slice 4 g + 2) lies behind a
-  // barrier, and the group's first read (slice 4 g + 4) behind the next.
-  template <bool ODD, int CUR, int DST, int PAR = 0>
-  __device__ __forceinline__ void convert_scales4(int t) {
-    const uint32_t keep0 = keep_mask(a.kb - 8 * t), keep1 = keep_mask(a.kb - 8 * t - 4);
-    u32x4(&cur)[4] = CUR == 0 ? sc_ck : sc_ckn;
-    u32x4(&nxt)[4] = CUR == 0 ? sc_ckn : sc_ck;
+  // fp4 scales.  Inside a slice (8 K blocks of 32 elements, 16 bytes of a
+  // row each), K step s of lane group g (lanes 16 g .. 16 g + 15) takes K
+  // block 2 g + s: the fragments read chunk 2 g + s of the slice (read_rows),
+  // and the scales of a lane for both K steps of a slice are then the
+  // consecutive bytes 2 g and 2 g + 1 of the row's 8 for the slice.  (Any
+  // assignment of the slice's K blocks to (K step, lane group) gives the
+  // same sum, as long as both operands and their scales follow it.)
+  //
+  // Rows whose scales start on a dword (kA4): the halfword is read from the
+  // staged group straight into the scale register of its block (byte s for
+  // K step s), no conversion.  Group g is loaded into registers in slice
+  // 4 g - 4, written to its slot after the next barrier, and read from
+  // slice 4 g - 1 on (the scales of slice t are read in slice t - 1).
+  __device__ __forceinline__ void load_group4(int g) {
+    const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w0 = ODD ? cur[j][2] : cur[j][0];
-      const uint32_t w1 = ODD ? cur[j][3] : cur[j][1];
-      const uint32_t w2 = ODD ? nxt[j][0] : cur[j][2];
-      const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sc_sh[j]) & keep0;
-      const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sc_sh[j]) & keep1;
-      const uint32_t lo = __builtin_amdgcn_perm(d1, d0, 0x05040100u);  // groups 0, 1, 4, 5
-      const uint32_t hi = __builtin_amdgcn_perm(d1, d0, 0x07060302u);  // groups 2, 3, 6, 7
-      // Block 2 j: lo of rows 0-31 in lanes 0-31, hi of the same rows in
-      // lanes 32-63; block 2 j + 1 likewise for rows 32-63.
-      const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
-      sc_set[DST][2 * j] = (int)sw[0];
-      sc_set[DST][2 * j + 1] = (int)sw[1];
+    for (int i = 0; i < 4; ++i)
+      sv4[i] = __builtin_amdgcn_raw_buffer_load_b128(r, st_off, (uint32_t)(2 * kChunkStride * g + 32 * i * a.kb), 0);
+  }
+  __device__ __forceinline__ void store_group4(int g) {
+    // The bytes stage_group would have written: chunk q of row 32 i + r of
+    // the wave's 128 at block 4 w + i, bytes 512 q + 16 r.
+    LDS_AS uint8_t *dst = slots.stage + (g & 1) * (512 * 32) + wave * 4096 + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(LDS_AS u32x4 *)(dst + i * 1024) = sv4[i];
+  }
+  // Pair u (slices 2 u, 2 u + 1) is converted like the other rows' below
+  // (each lane reads four rows and the lane groups exchange their dwords),
+  // without the realignment: the slot of group u / 2.  (Chosen between two
+  // pointers into the buffer rather than as an offset added to it: with an
+  // offset the compiler lost track of which LDS array the reads address,
+  // and made each wait for all the panel loads in flight.)
+  __device__ __forceinline__ void begin_pair4a(int u) {
+    sb4 = ((u >> 1) & 1) ? slots.stage + 512 * 32 : slots.stage;
+  }
+  // Row K (16 K + r of the lane's four 16-row blocks, in 32-row blocks of
+  // the slot) of chunk Q (= u % 2) of the group.
+  template <int K, int Q>
+  __device__ __forceinline__ void read_row4a() {
+    t4[K] = *(const LDS_AS u32x4 *)(sb4 + rd4 + Q * 512 + (K >> 1) * 1024 + (K & 1) * 256);
+  }
+
+  // Other rows (a dword may start inside a row's scales, or K not a
+  // multiple of the slice): chunk c of this wave's 128 rows into slot c % 3
+  // of a ring, converted per pair of slices (u: slices 2 u, 2 u + 1) into
+  // one dword per block with bytes 2 g, 2 g + 1 of slice 2 u and of slice
+  // 2 u + 1 (K step s of slice t at byte 2 (t % 2) + s).
+  __device__ __forceinline__ void stage_chunk4(int c) {
+    LDS_AS uint8_t *dst = slots.stage + (c % 3) * 8192 + wave * 2048;
+    const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)(dst + i * 1024), 16, st_off,
+                                               (uint32_t)(kChunkStride * c + 64 * i * a.kb), 0, 0);
+  }
+  // Pair u: the slot offsets of chunks u and u + 1, and the mask of the
+  // bytes of this lane's dwords that hold scale blocks of the row (blocks
+  // 16 u + 2 g + {0, 1, 8, 9} below kb).
+  __device__ __forceinline__ void begin_pair4(int u) {
+    cs4[0] = (uint32_t)((u % 3) * 8192);
+    cs4[1] = (uint32_t)(((u + 1) % 3) * 8192);
+    const int left = a.kb - 16 * u - 2 * (lane >> 4);
+    keep4 = (left > 0 ? 0xffu : 0u) | (left > 1 ? 0xff00u : 0u) | (left > 8 ? 0xff0000u : 0u) |
+            (left > 9 ? 0xff000000u : 0u);
+  }
+  // This lane's four rows (row r of blocks 4 g' .. 4 g' + 3 for lane group
+  // g'): chunk u and the first dword of chunk u + 1.  The reads are written
+  // out, with their wait, in one asm statement: as ordinary loads the
+  // compiler cannot tell them from the staging loads into the same buffer
+  // still in flight, and made them wait for every outstanding global load
+  // (about 10% of the K loop).  Every staging load they depend on was
+  // waited for by an earlier barrier.
+  __device__ __forceinline__ void read_scales4() {
+    const uint32_t p0 = (uint32_t)(uintptr_t)slots.stage + rd4 + cs4[0];
+    const uint32_t p1 = (uint32_t)(uintptr_t)slots.stage + rd4 + cs4[1];
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:256\n\t"
+        "ds_read_b128 %2, %8 offset:512\n\t"
+        "ds_read_b128 %3, %8 offset:768\n\t"
+        "ds_read_b32 %4, %9\n\t"
+        "ds_read_b32 %5, %9 offset:256\n\t"
+        "ds_read_b32 %6, %9 offset:512\n\t"
+        "ds_read_b32 %7, %9 offset:768\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t4[0]), "=&v"(t4[1]), "=&v"(t4[2]), "=&v"(t4[3]), "=&v"(t4n[0]), "=&v"(t4n[1]), "=&v"(t4n[2]),
+          "=&v"(t4n[3])
+        : "v"(p0), "v"(p1)
+        : "memory");
+  }
+  // Piece P (0, 1) of row K: its 16 bytes of the pair realigned to its
+  // first block (w0 .. w3, blocks 4 s .. 4 s + 3 in w_s), and the dword of
+  // lane group j: bytes 2 j, 2 j + 1, 8 + 2 j, 9 + 2 j, into slot j of the
+  // row's block (sc_set[SET][4 j + K]) until exchange4 hands it to lane
+  // group j.
+  template <int SET, int K, int P>
+  __device__ __forceinline__ void convert_scale4() {
+    const u32x4 &c = t4[K];
+    if constexpr (kA4) {
+      // Aligned rows: the chunk is the pair's 16 bytes.
+      if constexpr (P == 0) {
+        sc_set[SET][K] = (int)__builtin_amdgcn_perm(c[2], c[0], 0x05040100u);
+        sc_set[SET][4 + K] = (int)__builtin_amdgcn_perm(c[2], c[0], 0x07060302u);
+      } else {
+        sc_set[SET][8 + K] = (int)__builtin_amdgcn_perm(c[3], c[1], 0x05040100u);
+        sc_set[SET][12 + K] = (int)__builtin_amdgcn_perm(c[3], c[1], 0x07060302u);
+      }
+    } else if constexpr (P == 0) {
+      w4[0] = __builtin_amdgcn_alignbyte(c[1], c[0], sh4);
+      w4[1] = __builtin_amdgcn_alignbyte(c[2], c[1], sh4);
+      w4[2] = __builtin_amdgcn_alignbyte(c[3], c[2], sh4);
+      w4[3] = __builtin_amdgcn_alignbyte(t4n[K], c[3], sh4);
+    } else {
+      sc_set[SET][K] = (int)__builtin_amdgcn_perm(w4[2], w4[0], 0x05040100u);
+      sc_set[SET][4 + K] = (int)__builtin_amdgcn_perm(w4[2], w4[0], 0x07060302u);
+      sc_set[SET][8 + K] = (int)__builtin_amdgcn_perm(w4[3], w4[1], 0x05040100u);
+      sc_set[SET][12 + K] = (int)__builtin_amdgcn_perm(w4[3], w4[1], 0x07060302u);
     }
-    if constexpr (ODD)
-      fetch_chunk<PAR>(cur);
-    else if constexpr (PAR == 1)
-      stage_group(t / 4 + 1);
+  }
+  // Lane group g holds in slot j the dwords of lane group j for its blocks
+  // 4 g .. + 3; lane group j needs them in slot g.  A transpose of (lane
+  // group, slot) in two stages: the halves of the wave exchange slots 2-3
+  // against 0-1, then odd and even 16-lane rows exchange odd slots against
+  // even ones; after both, slot g of lane l holds its dwords for blocks
+  // 4 g .. 4 g + 3.  Swaps 2 Q and 2 Q + 1 of stage P.
+  template <int SET, int P, int Q>
+  __device__ __forceinline__ void exchange4() {
+#pragma unroll
+    for (int n = 2 * Q; n < 2 * Q + 2; ++n) {
+      const int h = n / 4, k = n % 4;
+      const int d = P == 0 ? 4 * h + k : 8 * h + k, e = P == 0 ? d + 8 : d + 4;
+      if constexpr (P == 0) {
+        const auto r = __builtin_amdgcn_permlane32_swap(sc_set[SET][d], sc_set[SET][e], false, false);
+        sc_set[SET][d] = (int)r[0];
+        sc_set[SET][e] = (int)r[1];
+      } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(sc_set[SET][d], sc_set[SET][e], false, false);
+        sc_set[SET][d] = (int)r[0];
+        sc_set[SET][e] = (int)r[1];
+      }
+    }
+  }
+  // Dwords 2 Q and 2 Q + 1 masked to the scale blocks of the row.
+  template <int SET, int Q>
+  __device__ __forceinline__ void mask4() {
+    sc_set[SET][2 * Q] &= (int)keep4;
+    sc_set[SET][2 * Q + 1] &= (int)keep4;
+  }
+  // Step N of a pair's conversion, one per MFMA: the four rows' reads (0),
+  // their conversion (4 + 2 K + P), the exchange (12-19) and the masks
+  // (20-27).
+  template <int SET, int N, int Q = 0>
+  __device__ __forceinline__ void pair4_step() {
+    if constexpr (kA4) {
+      // Aligned rows: reads (0-3), their conversion four MFMAs later (8-15),
+      // the exchange (16-23); whole blocks of the row, nothing to mask.
+      if constexpr (N < 4) read_row4a<N, Q>();
+      else if constexpr (N >= 8 && N < 16) convert_scale4<SET, (N - 8) / 2, (N - 8) % 2>();
+      else if constexpr (N >= 16 && N < 24) exchange4<SET, (N - 16) / 4, (N - 16) % 4>();
+    } else if constexpr (N == 0) read_scales4();
+    else if constexpr (N >= 4 && N < 12) convert_scale4<SET, (N - 4) / 2, (N - 4) % 2>();
+    else if constexpr (N >= 12 && N < 20) exchange4<SET, (N - 12) / 4, (N - 12) % 4>();
+    else if constexpr (N >= 20 && N < 28) mask4<SET, N - 20>();
+  }
+  static constexpr int kPair4Steps = 28;
+
+  // Every step at once (the prologue: pair 0 into set 0).
+  template <int... N>
+  __device__ __forceinline__ void convert_pair4(std::integer_sequence<int, N...>) {
+    (pair4_step<0, N, 0>(), ...);
   }
 
   // fp8: group g, shifted out of the window's first two dwords and
@@ -858,7 +1048,7 @@ struct Kernel {
     // ones), so the two MFMAs at each turn share their y operand: less
     // operand switching, 0.4% faster under the power cap at 4096 x 4096 x
     // 8192 bf16, 0.2-0.9% for the block-scaled kinds.
-    constexpr int H = q % kHalves, I = q / kHalves / kNBm, J0 = q / kHalves % kNBm;
+    constexpr int I = q / kNBm, J0 = q % kNBm;
     constexpr int J = (I & 1) ? kNBm - 1 - J0 : J0;
     constexpr int kHead = load_at(Q, false), kTail = load_at(Q, true);
     if constexpr (kFreeAt < kBarrierAt && Q == kFreeAt) {
@@ -876,14 +1066,38 @@ struct Kernel {
       if constexpr (kZeroTail)
         if (kt + 1 == zt) zero_tail<(S + 1) % kNS>(kt + 1);
       barrier();
-      // fp4: the scales of slice kt + 1 into the next set, from the chunk
-      // buffer that holds them (JB = kt % 4: slices 4 i + 2 and 4 i + 3 read
-      // sc_ck, 4 i + 4 and 4 i + 5 sc_ckn).  An odd slice ends its chunk,
-      // whose buffer then takes the chunk after the next (waited for by the
-      // next barrier, used after the one after).
-      // fp4: JB = kt % 4, the odd slice kt + 1 = 2 c + 1 has c % 2 = JB / 2.
-      if constexpr (T::kDt == kFp4)
-        convert_scales4<(JB & 1) == 0, JB == 1 || JB == 2 ? 0 : 1, (JB + 1) & 1, (JB >> 1) & 1>(kt + 1);
+      // fp4 (JB = kt % 4): in an even slice, every wave's reads of chunk
+      // kt / 2 - 1 lie behind this barrier, and chunk kt / 2 + 3 goes into
+      // its slot; the next barrier waits for it.
+      //    Aligned rows: at kt = 4 g - 1, group g + 1 is loaded into
+      //    registers; at kt = 4 g (this barrier waited for it) it goes into
+      //    the slot of group g - 1, whose last reads (pair 2 g - 1) were in
+      //    slice 4 g - 4; the barrier of slice 4 g + 1 publishes it for pair
+      //    2 g + 2, converted in slice 4 g + 2.
+      if constexpr (kA4) {
+        if constexpr (JB == 3) load_group4(((kt + 1) >> 2) + 1);
+        if constexpr (JB == 0) store_group4((kt >> 2) + 1);
+      } else if constexpr (T::kDt == kFp4) {
+        if constexpr ((JB & 1) == 0) stage_chunk4((kt >> 1) + 3);
+      }
+    }
+    if constexpr (T::kDt == kFp4 && (JB & 1) == 0) {
+      // An even slice kt converts the scales of the pair after the current
+      // one (u = kt / 2 + 1) into the set the previous pair used: chunks u
+      // and u + 1, staged and published by the barriers of slices kt - 2 and
+      // kt - 1 or earlier.  One step per MFMA, ending at the barrier; the
+      // reads (whose wait takes every LDS read in flight) go out several
+      // MFMAs after this slice's substep-1 fragment reads.
+      constexpr int N = Q - (kBarrierAt - kPair4Steps), SET = ((JB >> 1) + 1) & 1;
+      static_assert(kNRead + 1 + kPair4Steps <= kBarrierAt, "a pair's conversion fits before the barrier");
+      if constexpr (N == -1) {
+        if constexpr (kA4)
+          begin_pair4a((kt >> 1) + 1);
+        else
+          begin_pair4((kt >> 1) + 1);
+      }
+      // (Aligned rows: u = kt / 2 + 1 is odd for kt % 4 = 0, chunk 1 of its group.)
+      if constexpr (N >= 0 && N < kPair4Steps) pair4_step<SET, N, JB == 0 ? 1 : 0>();
     }
     if constexpr (Q < kNRead) read_piece<S, Q>(f1, 1);
     if constexpr (Q >= kBarrierAt && Q - kBarrierAt < kNRead) read_piece<(S + 1) % kNS, Q - kBarrierAt>(f0, 0);
@@ -891,9 +1105,11 @@ struct Kernel {
     if constexpr (kTail >= 0) load_one<S>(kt + kNS, kTail);
     if constexpr (kPfDist > 0 && Q == kPfAt) prefetch(kt + kPfDist);
     const Frags &f = SUB == 0 ? f0 : f1;
-    if constexpr (T::kDt == kFp4)
-      acc[I][J] = mma<FIRST && SUB == 0 && H == 0, 2 * SUB + H, H>(f.x[I], f.y[J], acc[I][J], sc_set[JB & 1][I],
-                                                                   sc_set[JB & 1][4 + J]);
+    if constexpr (T::kDt == kFp4) {
+      // A set per pair of slices (kt / 2 % 2), byte 2 (kt % 2) + SUB.
+      constexpr int SET4 = (JB >> 1) & 1, SEL4 = 2 * (JB & 1) + SUB;
+      acc[I][J] = mma<FIRST && SUB == 0, SEL4>(f.x[I], f.y[J], acc[I][J], sc_set[SET4][I], sc_set[SET4][kNBn + J]);
+    }
     else if constexpr (T::kScaled)
       acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
@@ -990,7 +1206,36 @@ struct Kernel {
           sc_off[j] = r < rows_valid ? (pos & ~3u) : kOOB;
           sc_sh[j] = pos & 3;
         }
-        if constexpr (kStaged) {
+        if constexpr (kA4) {
+          if (op == (wave >> 1)) {
+            // As fp6: rows r + 32, r + 64, r + 96 are 32 kb bytes apart.
+            const int r = (wave & 1) * 128 + (lane & 31);
+            const uint32_t pos = (uint32_t)r * (uint32_t)a.kb;
+            st_off = r < rows_valid ? pos + (uint32_t)(kChunkStride * (lane >> 5)) : kOOB;
+          }
+          // Lane 16 g + r reads rows 64 (g % 2) + 16 k + r of the wave's x
+          // rows (g < 2) or y rows: 32-row block op 8 + 4 wave + 2 (g % 2)
+          // + k / 2 of the slot, row 16 (k % 2) + r.
+          if (op == (lane >> 5)) {
+            const int blk = op * 8 + (op ? wave_m : wave_n) * 4 + 2 * ((lane >> 4) & 1);
+            rd4 = (uint32_t)(1024 * blk + 16 * (lane & 15));
+          }
+        } else if constexpr (T::kDt == kFp4) {
+          if (op == (wave >> 1)) {
+            // Row r + 64 is 64 kb bytes further, and so is its aligned
+            // offset.  (Past the last row the resource ends: zeros.)
+            const int r = (wave & 1) * 128 + lane;
+            const uint32_t pos = mis + (uint32_t)r * (uint32_t)a.kb;
+            st_off = r < rows_valid ? (pos & ~3u) : kOOB;
+          }
+          // Lane 16 g + r converts rows 64 (g % 2) + 16 k + r of the wave's
+          // x rows (g < 2) or y rows: 16 kb bytes apart, so one shift.
+          if (op == (lane >> 5)) {
+            const int r = (op ? wave_m : wave_n) * 128 + 64 * ((lane >> 4) & 1) + (lane & 15);
+            sh4 = (mis + (uint32_t)r * (uint32_t)a.kb) & 3;
+            rd4 = (uint32_t)(16 * ((op ? 256 : 0) + r));
+          }
+        } else if constexpr (kStaged) {
           if (op == (wave >> 1)) {
             // Rows r + 32, r + 64, r + 96 are 32 kb bytes apart each, and so
             // are their aligned offsets.
@@ -1000,10 +1245,13 @@ struct Kernel {
           }
         }
       }
+      if constexpr (T::kDt != kFp4) {
+        // (fp4 starts its accumulators from the MFMA's constant 0.)
 #pragma unroll
-      for (int i = 0; i < kNBn; ++i)
+        for (int i = 0; i < kNBn; ++i)
 #pragma unroll
-        for (int j = 0; j < kNBm; ++j) acc[i][j] = Acc{};
+          for (int j = 0; j < kNBm; ++j) acc[i][j] = Acc{};
+      }
     }
     if constexpr (T::kFp6)
       run6();
@@ -1015,12 +1263,16 @@ struct Kernel {
   // epilogue.
   __device__ __forceinline__ void run_slices() {
 
-    // Prologue: the first two scale chunks, slice 0 into slot 0, the loads
-    // of slice 1 that a previous slice's tail would have issued; wait for
-    // all but those, and convert slice 0's scales.  (With K = 0 every slice
-    // is all zeros.)
-    if constexpr (kStaged) {
-      stage_group(0);
+    // Prologue: the first scale chunks, slice 0 into slot 0, the loads of
+    // slice 1 that a previous slice's tail would have issued; wait for all
+    // but those, and convert slice 0's scales.  (With K = 0 every slice is
+    // all zeros.)
+    if constexpr (kA4) {
+      load_group4(0);
+    } else if constexpr (T::kDt == kFp4) {
+      stage_chunk4(0);
+      stage_chunk4(1);
+      stage_chunk4(2);
     } else if constexpr (T::kScaled) {
       load_chunks(sc_ck, 0);
       load_chunks(sc_ckn, 1);
@@ -1030,11 +1282,23 @@ struct Kernel {
 #pragma unroll
     for (int i = 0; i < kTailLoads; ++i) load_one<kNS - 1>(kNS - 1, i);
     wait_vm_lgkm0<(kNS - 2) * kLoads + kTailLoads>();
-    if constexpr (kStaged) {
-      // Every wave's staged group 0 is in LDS after this barrier.
+    if constexpr (kA4) {
+      // Group 0 into its slot (group 1 follows it into registers; slice 0's
+      // barrier stores it); every wave's part is in LDS after the barrier;
+      // then pair 0's scales into set 0.
+      store_group4(0);
+      // (The LDS writes may read their registers after a later load has
+      // started: wait for them before the registers take group 1.)
+      wait_vm_lgkm0<63>();
+      load_group4(1);
       barrier();
-      fetch_chunk<0>(sc_ckn);
-      fetch_chunk<1>(sc_ck);
+      begin_pair4a(0);
+      convert_pair4(std::make_integer_sequence<int, kPair4Steps>());
+    } else if constexpr (T::kDt == kFp4) {
+      // Every wave's staged chunks 0-2 are in LDS after this barrier.
+      barrier();
+      begin_pair4(0);
+      convert_pair4(std::make_integer_sequence<int, kPair4Steps>());
     }
     if constexpr (kZeroTail)
       if (zt == 0) zero_tail<0>(0);
@@ -1042,13 +1306,8 @@ struct Kernel {
       convert_scales(0);
 #pragma unroll
       for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
-    } else if constexpr (T::kDt == kFp4) {
-      convert_scales4<false, 1, 0>(0);
     }
     barrier();
-    // fp4: group 1 (chunks 2 and 3) over group 0, whose reads by every wave
-    // have completed before the barrier above.
-    if constexpr (T::kDt == kFp4) stage_group(1);
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
     // Slice 0 starts the accumulators; then the slices go round the ring a
@@ -1869,8 +2128,9 @@ hipError_t launch(const Problem &p) {
       break;
     case Dt::kMxfp4:
       if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
-        return p.K > 0 && p.K % 256 == 0 ? launch_shape<Traits<kFp4, true, true, true>, 256, 256>(p, a)
-                                         : launch_shape<Traits<kFp4, true, true>, 256, 256>(p, a);
+        return p.K > 0 && p.K % 256 == 0 && (((uintptr_t)a.SA | (uintptr_t)a.SB) & 3) == 0
+                   ? launch_shape<Traits<kFp4, true, true, true>, 256, 256>(p, a)
+                   : launch_shape<Traits<kFp4, true, true>, 256, 256>(p, a);
       break;
     case Dt::kMxfp6E2M3:
       if (tm == 256 && tn == 256 && !p.trans_a && p.trans_b)
