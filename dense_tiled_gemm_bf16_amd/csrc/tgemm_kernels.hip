@@ -39,9 +39,10 @@
 //    the barrier, overlapping the current slice's remaining MFMAs.  fp6:
 //    two slots of line stages, four barriers per 8 K steps.
 //  * wave-tile MMA: v_mfma_f32_16x16x32_{bf16,f16} (8 x 8 blocks per wave)
-//    and, for the block-scaled kinds, v_mfma_scale_f32_32x32x64_f8f6f4
-//    (4 x 4 blocks) with the e8m0 block scales as operands (TCGEN05
-//    tutorial, "进阶" (Advanced)), on fp8, fp6 or fp4 elements.
+//    and, for the block-scaled kinds, the scaled f8f6f4 MFMA with the e8m0
+//    block scales as operands (TCGEN05 tutorial, "进阶" (Advanced)):
+//    32 x 32 x 64 (4 x 4 blocks) on fp8 and fp6 elements, 16 x 16 x 128
+//    (8 x 8 blocks) on fp4.
 //  * operand layouts (trans_A / trans_B of the SM100 README's T.gemm): an
 //    operand stored K-contiguous (A as M x K, B as N x K) is staged row by
 //    row as above; one stored M- or N-contiguous (A as K x M, B as K x N)
@@ -148,13 +149,16 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // passes; for gfx950 the compiler's own hazard recognizer places, for the
 // builtins of the forms used here, 8 wait states after
 // v_mfma_f32_16x16x32_bf16/_f16 (4 passes), 12 after the scaled 32 x 32 x 64
-// form on fp4/fp6 (8 passes) and 20 after it on fp8 (16 passes) before a
-// dependent v_mul_f32 (checked on this build's own assembly).  Three
-// s_nop 7 give 24.  Between MFMAs no states are needed: consecutive MFMAs
-// write different accumulators, an accumulator is read again as SrcC only
-// by the same form 64 (16-bit) or 16 (scaled) MFMAs later, and the fragment
-// registers an MFMA reads (SrcA/B, read in its first pass) are rewritten
-// only by LDS reads issued after it, whose data returns tens of cycles later.
+// form on fp6 (8 passes) and 20 after it on fp8 (16 passes) before a
+// dependent v_mul_f32 (checked on this build's own assembly); the scaled
+// 16 x 16 x 128 form on fp4 (4 passes, also inline asm) needs no more than
+// the 32 x 32 x 64 one.  Three s_nop 7 give 24.  Between MFMAs no states
+// are needed: consecutive MFMAs write different accumulators, an
+// accumulator is read again as SrcC only by the same form 64 (16 x 16
+// blocks) or 16 (32 x 32) MFMAs later, the fragment registers an MFMA reads
+// (SrcA/B, read in its first pass) are rewritten only by LDS reads issued
+// after it, whose data returns tens of cycles later, and the fp4 scale
+// registers are rewritten at least a slice after their last MFMA.
 __device__ __forceinline__ void mfma_fence() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -346,7 +350,7 @@ struct Slots {
   LDS_AS uint8_t *a[4];
   LDS_AS uint8_t *b[4];
   LDS_AS uint8_t *junk;      // 256 bytes per wave: landing area of the L2 prefetches
-  LDS_AS uint8_t *stage;     // fp4, fp6: two 16-byte scale chunks for each of the 512 rows
+  LDS_AS uint8_t *stage;     // fp4, fp6: staged 16-byte scale chunks of the 512 rows
 };
 
 
@@ -401,7 +405,9 @@ struct Kernel {
   static_assert(kNR <= kBarrierAt, "this slice's second-substep reads come before the barrier");
   static_assert(kWindow <= kMfma && kWindow >= kLoads, "load window");
 
-  // L2 prefetch (fp8 only).  A slice's lines are first touched by its loads
+  // L2 prefetch (fp8, and fp4 whose scale rows are not dword-aligned; the
+  // aligned fp4 kernel needs the LDS area for its scales and measured no
+  // slower without it).  A slice's lines are first touched by its loads
   // into LDS, which have about one slice to land.  For fp8, whose slices
   // hold twice the flops of the 16-bit kinds' 64-element slices but whose
   // loads are half issued in the slice before the barrier that waits for
@@ -468,17 +474,14 @@ struct Kernel {
   // from the dword holding the row's first scale byte, plus 16 c.  Any 4
   // consecutive bytes of the row that start in chunk c can be shifted out
   // of it and the next chunk's first dword, so two chunks are kept.  A
-  // chunk covers 16 slices of fp8 (one scale per 128 K) or 2 of fp4 (8 per
-  // 256-element slice).  Loading a row's bytes 16 at a time keeps the
-  // texture unit's work small: each of these loads touches 64 cache lines
-  // (one per lane), as many as a 1 KB panel load touches bytes / 16.
+  // chunk covers 16 slices of fp8 (one scale per 128 K).  Loading a row's
+  // bytes 16 at a time keeps the texture unit's work small: each of these
+  // loads touches 64 cache lines (one per lane), as many as a 1 KB panel
+  // load touches bytes / 16.  (fp4 and fp6 stage their chunks instead,
+  // below.)
   //  * fp8: group g (slices 4 g .. 4 g + 3) is one shifted dword, handed
   //    to the lanes that feed that row to the MFMA; the MFMA's byte select
   //    then picks the slice.
-  //  * fp4: slice t is two shifted dwords (groups 0-3, 4-7); the MFMA of
-  //    substep s, half h of a lane in wave half w uses group 4 s + 2 w + h,
-  //    so lanes 0-31 take groups 0, 1, 4, 5 and lanes 32-63 groups 2, 3, 6,
-  //    7, in byte 2 s + h.
   // Bytes past the row's last scale block (the next row's, in a padded
   // slice) are zeroed: the slices they would scale hold zeros, and a NaN
   // scale (0xff) would turn those zeros into NaN.
@@ -501,7 +504,8 @@ struct Kernel {
   //    4 w + i: chunk q of row 32 i + r of the wave's 128 at bytes 512 q +
   //    16 r.
   //  * fp4 with dword-aligned scale rows: groups as for fp6, in two 16 KiB
-  //    slots (group g in slot g % 2); pair u of slices takes chunk u % 2 of
+  //    slots (group g in slot g % 2), written from registers (sv4) rather
+  //    than loaded into LDS directly; pair u of slices takes chunk u % 2 of
   //    group u / 2.
   //  * other fp4: one chunk at a time into a ring of three 8 KiB slots (chunk c
   //    in slot c % 3), row R of the tile (B rows 0-255, then A rows) at
@@ -511,9 +515,9 @@ struct Kernel {
   //    does not start on a dword).  st_off: this lane's row in the first
   //    instruction (aligned byte offset, or kOOB).
   static constexpr bool kStaged = T::kDt == kFp4 || T::kFp6;
-  // fp4 with dword-aligned scale rows: two slots of groups (as fp6 stages
-  // them), pair u in chunk u % 2 of group u / 2.  (The L2 prefetch area goes
-  // to make room: 128 + 32 KiB fill the LDS.)
+  // fp4 with dword-aligned scale rows: two slots of groups, pair u in chunk
+  // u % 2 of group u / 2.  (The L2 prefetch area goes to make room: 128 +
+  // 32 KiB fill the LDS.)
   static constexpr bool kA4 = T::kDt == kFp4 && T::kWholeK;
   static constexpr int kStageBytes = kA4 ? 2 * 512 * 32 : T::kDt == kFp4 ? 3 * 512 * 16 : 512 * 32;
   static constexpr int kChunkStride = 16;  // row bytes between consecutive chunks
@@ -532,11 +536,11 @@ struct Kernel {
   uint32_t w4[4];  // one row's realigned dwords
   u32x4 sv4[4];    // aligned rows: a group on its way from the L2 to its slot
   const LDS_AS uint8_t *sb4;  // aligned rows: the slot of the pair being converted
-  // Per block (4 x blocks, then 4 y blocks): fp8, the bytes of a group of 4
+  // Per block (x blocks, then y blocks): fp8, the bytes of a group of 4
   // slices, converted into sc_nxt and copied into sc_cur before the group's
-  // first slice.  fp4 and fp6 convert every slice's scales straight into
-  // the set its MFMAs read (fp4: set kt % 2; fp6: set (k / 2) % 2 for K step
-  // k), so no copy is needed at the start of a slice.
+  // first slice.  fp4 and fp6 convert their scales straight into the set
+  // their MFMAs read (fp4: set (kt / 2) % 2 for a pair of slices; fp6: set
+  // (k / 2) % 2 for K step k), so no copy is needed at the start of a slice.
   int sc_nxt[8], sc_cur[8];
   int sc_set[2][kNR];
   Acc acc[kNBn][kNBm];
@@ -1066,9 +1070,9 @@ struct Kernel {
       if constexpr (kZeroTail)
         if (kt + 1 == zt) zero_tail<(S + 1) % kNS>(kt + 1);
       barrier();
-      // fp4 (JB = kt % 4): in an even slice, every wave's reads of chunk
-      // kt / 2 - 1 lie behind this barrier, and chunk kt / 2 + 3 goes into
-      // its slot; the next barrier waits for it.
+      // fp4 (JB = kt % 4), rows not dword-aligned: in an even slice, every
+      // wave's reads of chunk kt / 2 - 1 lie behind this barrier, and chunk
+      // kt / 2 + 3 goes into its slot; the next barrier waits for it.
       //    Aligned rows: at kt = 4 g - 1, group g + 1 is loaded into
       //    registers; at kt = 4 g (this barrier waited for it) it goes into
       //    the slot of group g - 1, whose last reads (pair 2 g - 1) were in
