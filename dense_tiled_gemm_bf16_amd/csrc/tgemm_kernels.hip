@@ -533,7 +533,7 @@ struct Kernel {
   uint32_t keep4, cs4[2];
   u32x4 t4[4];
   uint32_t t4n[4];
-  uint32_t w4[4];  // one row's realigned dwords
+  uint32_t w4[4], e4[4];  // one row's realigned dwords and their byte pairs
   u32x4 sv4[4];    // aligned rows: a group on its way from the L2 to its slot
   const LDS_AS uint8_t *sb4;  // aligned rows: the slot of the pair being converted
   // Per block (x blocks, then y blocks): fp8, the bytes of a group of 4
@@ -563,12 +563,10 @@ struct Kernel {
       return r;
     } else {
       // 16 x 16 x 32: lane l holds row l % 16 and 8 elements of K: logical
-      // chunk 4 sub + l / 16.  fp4, 16 x 16 x 128: 32 elements (one K block
-      // of 16 bytes), chunk 2 (l / 16) + sub (the K block order of the fp4
-      // scales, below).
+      // chunk 4 sub + l / 16.  (fp4, 16 x 16 x 128: 32 elements, one K
+      // block of 16 bytes, the same chunk.)
       const LDS_AS uint8_t *p = slot + (row0 + (lane & 15)) * kRowBytes;
-      const int c = T::kDt == kFp4 ? 2 * (lane >> 4) + sub : 4 * sub + (lane >> 4);
-      return *(const LDS_AS u32x4 *)(p + ((c ^ lane_sw) << 4));
+      return *(const LDS_AS u32x4 *)(p + (((4 * sub + (lane >> 4)) ^ lane_sw) << 4));
     }
   }
 
@@ -845,17 +843,19 @@ struct Kernel {
 
   // fp4 scales.  Inside a slice (8 K blocks of 32 elements, 16 bytes of a
   // row each), K step s of lane group g (lanes 16 g .. 16 g + 15) takes K
-  // block 2 g + s: the fragments read chunk 2 g + s of the slice (read_rows),
-  // and the scales of a lane for both K steps of a slice are then the
-  // consecutive bytes 2 g and 2 g + 1 of the row's 8 for the slice.  (Any
-  // assignment of the slice's K blocks to (K step, lane group) gives the
-  // same sum, as long as both operands and their scales follow it.)
+  // block 4 s + g; over a pair of slices (u: slices 2 u, 2 u + 1) K step
+  // s = 2 (t % 2) + sub of slice t takes block 16 u + 4 s + g of the row,
+  // byte s of the lane's scale dword for its block: bytes g, g + 4, g + 8,
+  // g + 12 of the row's 16 for the pair, a column of the 4 x 4 byte matrix
+  // they form.  Each lane converts four rows (all four columns of each) and
+  // the lane groups then exchange the columns (exchange4).  (The order with
+  // each lane group's two blocks of a slice side by side, 2 g + s, needed
+  // no transpose but made the fragment reads conflict in LDS banks, half of
+  // their cycles.)
   //
-  // Rows whose scales start on a dword (kA4): the halfword is read from the
-  // staged group straight into the scale register of its block (byte s for
-  // K step s), no conversion.  Group g is loaded into registers in slice
-  // 4 g - 4, written to its slot after the next barrier, and read from
-  // slice 4 g - 1 on (the scales of slice t are read in slice t - 1).
+  // Rows whose scales start on a dword (kA4): groups of two chunks staged
+  // through registers.  Group g + 1 is loaded in slice 4 g - 1, written to
+  // its slot after the next barrier and published by the one after.
   __device__ __forceinline__ void load_group4(int g) {
     const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
 #pragma unroll
@@ -887,9 +887,7 @@ struct Kernel {
 
   // Other rows (a dword may start inside a row's scales, or K not a
   // multiple of the slice): chunk c of this wave's 128 rows into slot c % 3
-  // of a ring, converted per pair of slices (u: slices 2 u, 2 u + 1) into
-  // one dword per block with bytes 2 g, 2 g + 1 of slice 2 u and of slice
-  // 2 u + 1 (K step s of slice t at byte 2 (t % 2) + s).
+  // of a ring; a pair's 16 bytes of a row start inside chunk u.
   __device__ __forceinline__ void stage_chunk4(int c) {
     LDS_AS uint8_t *dst = slots.stage + (c % 3) * 8192 + wave * 2048;
     const __amdgpu_buffer_rsrc_t r = (wave >> 1) ? rss[1] : rss[0];
@@ -899,14 +897,13 @@ struct Kernel {
                                                (uint32_t)(kChunkStride * c + 64 * i * a.kb), 0, 0);
   }
   // Pair u: the slot offsets of chunks u and u + 1, and the mask of the
-  // bytes of this lane's dwords that hold scale blocks of the row (blocks
-  // 16 u + 2 g + {0, 1, 8, 9} below kb).
+  // bytes of this lane's dwords that hold scale blocks of the row (byte s:
+  // block 16 u + 4 s + g below kb).
   __device__ __forceinline__ void begin_pair4(int u) {
     cs4[0] = (uint32_t)((u % 3) * 8192);
     cs4[1] = (uint32_t)(((u + 1) % 3) * 8192);
-    const int left = a.kb - 16 * u - 2 * (lane >> 4);
-    keep4 = (left > 0 ? 0xffu : 0u) | (left > 1 ? 0xff00u : 0u) | (left > 8 ? 0xff0000u : 0u) |
-            (left > 9 ? 0xff000000u : 0u);
+    const int left = a.kb - 16 * u - (lane >> 4);
+    keep4 = keep_mask(left <= 0 ? 0 : (left + 3) >> 2);
   }
   // This lane's four rows (row r of blocks 4 g' .. 4 g' + 3 for lane group
   // g'): chunk u and the first dword of chunk u + 1.  The reads are written
@@ -933,33 +930,45 @@ struct Kernel {
         : "v"(p0), "v"(p1)
         : "memory");
   }
-  // Piece P (0, 1) of row K: its 16 bytes of the pair realigned to its
-  // first block (w0 .. w3, blocks 4 s .. 4 s + 3 in w_s), and the dword of
-  // lane group j: bytes 2 j, 2 j + 1, 8 + 2 j, 9 + 2 j, into slot j of the
-  // row's block (sc_set[SET][4 j + K]) until exchange4 hands it to lane
-  // group j.
+  // Piece P (0-3) of row K: the dword of lane group j, bytes j, j + 4,
+  // j + 8, j + 12 of the row's 16 for the pair, into slot j of the row's
+  // block (sc_set[SET][4 j + K]) until exchange4 hands it to lane group j.
   template <int SET, int K, int P>
   __device__ __forceinline__ void convert_scale4() {
     const u32x4 &c = t4[K];
+    // w0 .. w3: the row's 16 bytes of the pair (realigned to its first
+    // block unless aligned); e0 .. e3 pair up the bytes of w0, w1 and of
+    // w2, w3; column j = (w0.j, w1.j, w2.j, w3.j).  At most three VALU
+    // instructions per piece, so that each fits beside one MFMA.
     if constexpr (kA4) {
-      // Aligned rows: the chunk is the pair's 16 bytes.
       if constexpr (P == 0) {
-        sc_set[SET][K] = (int)__builtin_amdgcn_perm(c[2], c[0], 0x05040100u);
-        sc_set[SET][4 + K] = (int)__builtin_amdgcn_perm(c[2], c[0], 0x07060302u);
-      } else {
-        sc_set[SET][8 + K] = (int)__builtin_amdgcn_perm(c[3], c[1], 0x05040100u);
-        sc_set[SET][12 + K] = (int)__builtin_amdgcn_perm(c[3], c[1], 0x07060302u);
+        e4[0] = __builtin_amdgcn_perm(c[1], c[0], 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
+        e4[1] = __builtin_amdgcn_perm(c[1], c[0], 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
+      } else if constexpr (P == 1) {
+        e4[2] = __builtin_amdgcn_perm(c[3], c[2], 0x05010400u);
+        e4[3] = __builtin_amdgcn_perm(c[3], c[2], 0x07030602u);
       }
     } else if constexpr (P == 0) {
       w4[0] = __builtin_amdgcn_alignbyte(c[1], c[0], sh4);
       w4[1] = __builtin_amdgcn_alignbyte(c[2], c[1], sh4);
       w4[2] = __builtin_amdgcn_alignbyte(c[3], c[2], sh4);
+    } else if constexpr (P == 1) {
       w4[3] = __builtin_amdgcn_alignbyte(t4n[K], c[3], sh4);
-    } else {
-      sc_set[SET][K] = (int)__builtin_amdgcn_perm(w4[2], w4[0], 0x05040100u);
-      sc_set[SET][4 + K] = (int)__builtin_amdgcn_perm(w4[2], w4[0], 0x07060302u);
-      sc_set[SET][8 + K] = (int)__builtin_amdgcn_perm(w4[3], w4[1], 0x05040100u);
-      sc_set[SET][12 + K] = (int)__builtin_amdgcn_perm(w4[3], w4[1], 0x07060302u);
+      e4[0] = __builtin_amdgcn_perm(w4[1], w4[0], 0x05010400u);
+      e4[1] = __builtin_amdgcn_perm(w4[1], w4[0], 0x07030602u);
+    }
+    if constexpr (!kA4 && P == 2) {
+      e4[2] = __builtin_amdgcn_perm(w4[3], w4[2], 0x05010400u);
+      e4[3] = __builtin_amdgcn_perm(w4[3], w4[2], 0x07030602u);
+      sc_set[SET][K] = (int)__builtin_amdgcn_perm(e4[2], e4[0], 0x05040100u);
+    } else if constexpr (kA4 && P == 2) {
+      sc_set[SET][K] = (int)__builtin_amdgcn_perm(e4[2], e4[0], 0x05040100u);
+      sc_set[SET][4 + K] = (int)__builtin_amdgcn_perm(e4[2], e4[0], 0x07060302u);
+    }
+    if constexpr (P == 3) {
+      if constexpr (!kA4) sc_set[SET][4 + K] = (int)__builtin_amdgcn_perm(e4[2], e4[0], 0x07060302u);
+      sc_set[SET][8 + K] = (int)__builtin_amdgcn_perm(e4[3], e4[1], 0x05040100u);
+      sc_set[SET][12 + K] = (int)__builtin_amdgcn_perm(e4[3], e4[1], 0x07060302u);
     }
   }
   // Lane group g holds in slot j the dwords of lane group j for its blocks
@@ -992,22 +1001,22 @@ struct Kernel {
     sc_set[SET][2 * Q + 1] &= (int)keep4;
   }
   // Step N of a pair's conversion, one per MFMA: the four rows' reads (0),
-  // their conversion (4 + 2 K + P), the exchange (12-19) and the masks
-  // (20-27).
+  // their conversion (4 + 4 K + P), the exchange (20-27) and the masks
+  // (28-35).
   template <int SET, int N, int Q = 0>
   __device__ __forceinline__ void pair4_step() {
     if constexpr (kA4) {
-      // Aligned rows: reads (0-3), their conversion four MFMAs later (8-15),
-      // the exchange (16-23); whole blocks of the row, nothing to mask.
+      // Aligned rows: reads (0-3), their conversion four MFMAs later (8-23),
+      // the exchange (24-31); whole blocks of the row, nothing to mask.
       if constexpr (N < 4) read_row4a<N, Q>();
-      else if constexpr (N >= 8 && N < 16) convert_scale4<SET, (N - 8) / 2, (N - 8) % 2>();
-      else if constexpr (N >= 16 && N < 24) exchange4<SET, (N - 16) / 4, (N - 16) % 4>();
+      else if constexpr (N >= 8 && N < 24) convert_scale4<SET, (N - 8) / 4, (N - 8) % 4>();
+      else if constexpr (N >= 24 && N < 32) exchange4<SET, (N - 24) / 4, (N - 24) % 4>();
     } else if constexpr (N == 0) read_scales4();
-    else if constexpr (N >= 4 && N < 12) convert_scale4<SET, (N - 4) / 2, (N - 4) % 2>();
-    else if constexpr (N >= 12 && N < 20) exchange4<SET, (N - 12) / 4, (N - 12) % 4>();
-    else if constexpr (N >= 20 && N < 28) mask4<SET, N - 20>();
+    else if constexpr (N >= 4 && N < 20) convert_scale4<SET, (N - 4) / 4, (N - 4) % 4>();
+    else if constexpr (N >= 20 && N < 28) exchange4<SET, (N - 20) / 4, (N - 20) % 4>();
+    else if constexpr (N >= 28 && N < 36) mask4<SET, N - 28>();
   }
-  static constexpr int kPair4Steps = 28;
+  static constexpr int kPair4Steps = 36;
 
   // Every step at once (the prologue: pair 0 into set 0).
   template <int... N>
