@@ -46,7 +46,10 @@ def oracle_full(x):
     return oracle.gemm_mxfp4_nt(x["qA"], x["qB"], x["sA"], x["sB"])
 
 
-@pytest.mark.parametrize("K", [32, 96, 256, 288, 800])
+# K = 256, 768, 1280, 2560 take the kernel for dword-aligned scale rows (K a
+# multiple of 256): one slice, and odd numbers of slices whose last pair of
+# slices is half outside K; the others the kernel for any scale rows.
+@pytest.mark.parametrize("K", [32, 96, 256, 288, 768, 800, 1280, 2560])
 def test_tails(K):
     for M in [1, 31, 257, 300]:
         for N in [8, 56, 264]:
@@ -83,6 +86,27 @@ def test_unaligned_scale_pointers(offset):
 
     assert_bitwise(run(x, M, N, K, at_offset(x["sA"]), at_offset(x["sB"])), oracle_full(x),
                    f"mxfp4 scales at offset {offset}")
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_whole_slices_with_unaligned_scale_pointers(offset):
+    """K a multiple of 256 (32 scale blocks per row, whole dwords), the scale
+    arrays at offset 0 (the kernel for dword-aligned scale rows) or 1, 2
+    bytes past a dword (the kernel for any scale rows, chosen by the host
+    for the same K).  Bitwise on integer elements with varied scales."""
+    M, N, K = 264, 200, 1024
+    x = workloads.make_integer("mxfp4_nt", M, N, K, seed=70 + offset)
+    rng = np.random.default_rng(70 + offset)
+    x["sA"] = rng.integers(124, 131, x["sA"].shape).astype(np.uint8)
+    x["sB"] = rng.integers(124, 131, x["sB"].shape).astype(np.uint8)
+
+    def at_offset(bits):
+        buf = torch.zeros(bits.size + 4, dtype=torch.uint8, device="cuda")
+        buf[offset:offset + bits.size] = torch.from_numpy(np.ascontiguousarray(bits).reshape(-1)).cuda()
+        return buf[offset:offset + bits.size].view(bits.shape)
+
+    assert_bitwise(run(x, M, N, K, at_offset(x["sA"]), at_offset(x["sB"])), oracle_full(x),
+                   f"mxfp4 K={K} scales at offset {offset}")
 
 
 @pytest.mark.parametrize("offset", [0, 1, 3])
