@@ -149,16 +149,19 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // passes; for gfx950 the compiler's own hazard recognizer places, for the
 // builtins of the forms used here, 8 wait states after
 // v_mfma_f32_16x16x32_bf16/_f16 (4 passes), 12 after the scaled 32 x 32 x 64
-// form on fp6 (8 passes) and 20 after it on fp8 (16 passes) before a
-// dependent v_mul_f32 (checked on this build's own assembly); the scaled
-// 16 x 16 x 128 form on fp4 (4 passes, also inline asm) needs no more than
-// the 32 x 32 x 64 one.  Three s_nop 7 give 24.  Between MFMAs no states
-// are needed: consecutive MFMAs write different accumulators, an
-// accumulator is read again as SrcC only by the same form 64 (16 x 16
-// blocks) or 16 (32 x 32) MFMAs later, the fragment registers an MFMA reads
-// (SrcA/B, read in its first pass) are rewritten only by LDS reads issued
-// after it, whose data returns tens of cycles later, and the fp4 scale
-// registers are rewritten at least a slice after their last MFMA.
+// form on fp6 (8 passes) and 12 after the scaled 16 x 16 x 128 form on fp8
+// (8 passes) before a dependent v_mul_f32 (checked on this build's own
+// assembly); the scaled 16 x 16 x 128 form on fp4 (4 passes) needs no more.
+// Three s_nop 7 give 24.  Between MFMAs no states are needed: consecutive
+// MFMAs write different accumulators, an accumulator is read again as SrcC
+// only by the same form 64 (16 x 16 blocks) or 16 (32 x 32) MFMAs later,
+// the fragment registers an MFMA reads (SrcA/B, read in its first pass)
+// are rewritten only by LDS reads issued after it, whose data returns tens
+// of cycles later, the fp4 scale registers are rewritten at least a slice
+// after their last MFMA, and the fp8 ones after their last MFMA of a group
+// (the one write-after-read hazard of an MFMA is on SrcC) and at least two
+// MFMAs before the next MFMA that reads them (the two wait states a VALU
+// write needs before an MFMA reads the register).
 __device__ __forceinline__ void mfma_fence() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -354,6 +357,101 @@ struct Slots {
 };
 
 
+// fp8 K loop (the scaled 16 x 16 x 128 MFMA, one K step per slice, 8 x 8
+// blocks of 16 x 16 per wave): the order of a slice's 64 MFMAs and the
+// positions of the fragment reads.  A slice runs four quadrants of 4 x 4
+// blocks (x blocks 0-3 or 4-7 against y blocks 0-3 or 4-7), x block by x
+// block with the y blocks snaking, each quadrant's x blocks in the reverse
+// order of the one before, so that every MFMA shares an operand with the
+// one before it.  Slices of phase 0 (even) take the quadrants (x lo, y lo),
+// (x lo, y hi), (x hi, y hi), (x hi, y lo); slices of phase 1 (x lo, y hi),
+// (x lo, y lo), (x hi, y lo), (x hi, y hi).  Either way each group of
+// fragments is free (its last MFMA issued) 16 MFMAs or more before the next
+// slice first takes it, so the reads of the next slice's fragments spread
+// over the second half of a slice and the first of the next.
+namespace f8 {
+constexpr int kNB = 8;         // blocks per wave and dimension
+constexpr int kM = kNB * kNB;  // MFMAs per slice
+struct IJ {
+  int i, j;  // x block, y block
+};
+constexpr IJ order(int p, int q) {
+  const int k = q / 16, r = q % 16;
+  const int xh = k >= 2 ? 1 : 0;
+  const int yh = p ? (k == 0 || k == 3 ? 1 : 0) : (k == 1 || k == 2 ? 1 : 0);
+  const int xi = (k & 1) ? 3 - r / 4 : r / 4;
+  const int yi = ((r / 4) & 1) ? 3 - r % 4 : r % 4;
+  return IJ{4 * xh + xi, 4 * yh + yi};
+}
+// Fragment F: x block F (F < 8) or y block F - 8.
+constexpr bool uses(int p, int q, int F) { return F < kNB ? order(p, q).i == F : order(p, q).j == F - kNB; }
+constexpr int last_use(int p, int F) {
+  int l = -1;
+  for (int q = 0; q < kM; ++q)
+    if (uses(p, q, F)) l = q;
+  return l;
+}
+constexpr int first_use(int p, int F) {
+  for (int q = 0; q < kM; ++q)
+    if (uses(p, q, F)) return q;
+  return kM;
+}
+// Read positions for the next slice's fragments during a slice of phase p
+// (before MFMA pos of this slice; kM and on: of the next slice): each
+// fragment once its registers are free (after its last MFMA here) and the
+// barrier before MFMA `bar` has published the next slice, in order of
+// availability, at least `gap` MFMAs apart (a fragment is two 16-byte LDS
+// reads per lane; the LDS also takes the loads of the slice after).
+struct Sched {
+  int pos[2 * kNB];
+};
+constexpr int kGap = 2;
+constexpr Sched schedule(int p, int bar) {
+  Sched s{};
+  bool done[2 * kNB] = {};
+  int ready[2 * kNB] = {};
+  for (int F = 0; F < 2 * kNB; ++F) {
+    const int r = last_use(p, F) + 1;
+    ready[F] = r < bar ? bar : r;
+  }
+  int next = 0;
+  for (int n = 0; n < 2 * kNB; ++n) {
+    int best = -1, best_r = 0;
+    for (int F = 0; F < 2 * kNB; ++F)
+      if (!done[F] && (best < 0 || ready[F] < best_r)) {
+        best = F;
+        best_r = ready[F];
+      }
+    done[best] = true;
+    next = best_r > next ? best_r : next;
+    s.pos[best] = next;
+    next += kGap;
+  }
+  return s;
+}
+// Every read lands before the next slice's barrier and at least four
+// MFMAs before its first use there.
+constexpr bool schedule_ok(int bar) {
+  for (int p = 0; p < 2; ++p) {
+    const Sched s = schedule(p, bar);
+    for (int F = 0; F < 2 * kNB; ++F)
+      if (s.pos[F] >= kM + bar || s.pos[F] + 4 > kM + first_use(p ^ 1, F)) return false;
+  }
+  return true;
+}
+// A conversion at position pos of a slice of phase 1 (kM and on: of the
+// next slice, phase 0) writes the scale registers of blocks 4 J .. 4 J + 3
+// (x blocks for J < 2, y blocks after): after their last MFMA in the one
+// and at least two MFMAs before their first in the other.
+constexpr bool convert_ok(int pos, int J) {
+  for (int c = 0; c < 4; ++c) {
+    const int F = 4 * J + c;
+    if (pos <= last_use(1, F) || pos + 2 > kM + first_use(0, F)) return false;
+  }
+  return true;
+}
+}  // namespace f8
+
 template <class T, int TM, int TN, bool SPLIT = false>
 struct Kernel {
   static_assert(!SPLIT || !T::kScaled, "the K split is for the 16-bit kinds");
@@ -370,9 +468,11 @@ struct Kernel {
   // form for the same reason (in a register-only stream of random operands
   // under the power limit it delivered 13% more flops per second than the
   // 32 x 32 x 64 form); its 16-byte fragments are laid out like the 16-bit
-  // kinds'.  fp8: the scaled 32 x 32 x 64 form.  Either way a slice is two K
-  // substeps.
-  static constexpr bool kW = T::kScaled && T::kDt != kFp4;  // 32 x 32 blocks
+  // kinds'.  Their slices are two K substeps.  fp8: the scaled 16 x 16 x 128
+  // form too (9% more flops per second than 32 x 32 x 64 in the same
+  // stream), one K step per slice, in a K loop of its own (below).  fp6:
+  // the scaled 32 x 32 x 64 form, in its own K loop.
+  static constexpr bool kW = T::kFp6;  // 32 x 32 blocks
   static constexpr int kBlk = kW ? 32 : 16;
   static constexpr int kNBm = kWM / kBlk;       // blocks per wave along M (y blocks)
   static constexpr int kNBn = kWN / kBlk;       // blocks per wave along N (x blocks)
@@ -393,11 +493,11 @@ struct Kernel {
   // too short a window overrun the texture unit (about 64 bytes per clock
   // per CU) and stall the MFMA stream behind a full queue.  The barrier
   // positions are the measured best (fewest cycles per workgroup): halfway
-  // for the 128-MFMA 16-bit slice, three quarters for the 32-MFMA fp8 slice;
-  // halfway with loads spread over three quarters of a slice for fp4 and
-  // fp6 (about 3% fewer cycles than three quarters and a half).
+  // for the 128-MFMA 16-bit slice; halfway with loads spread over three
+  // quarters of a slice for fp4 (about 3% fewer cycles than three quarters
+  // and a half).  (fp8 and fp6 have K loops of their own.)
   static constexpr bool kFp46 = T::kDt == kFp4 || T::kFp6;
-  static constexpr int kBarrierAt = T::kDt == kFp8 ? kMfma * 3 / 4 : kMfma / 2;
+  static constexpr int kBarrierAt = kMfma / 2;
   static constexpr int kFreeAt = kBarrierAt;
   static constexpr int kWindow = kFp46 ? kMfma * 3 / 4 : kMfma / 2;
   static_assert(kFreeAt >= kNR && kFreeAt <= kBarrierAt, "slot-free barrier after this slice's reads");
@@ -408,17 +508,16 @@ struct Kernel {
   // L2 prefetch (fp8, and fp4 whose scale rows are not dword-aligned; the
   // aligned fp4 kernel needs the LDS area for its scales and measured no
   // slower without it).  A slice's lines are first touched by its loads
-  // into LDS, which have about one slice to land.  For fp8, whose slices
-  // hold twice the flops of the 16-bit kinds' 64-element slices but whose
-  // loads are half issued in the slice before the barrier that waits for
-  // them, one dword of every 128-byte line of slice kt + kPfDist is loaded
-  // early (into a scratch LDS area, no registers), right after the last LDS
-  // load that the next barrier waits for: that barrier waits with
-  // vmcnt(1), and the prefetch has until the barrier after it, about 1.5
-  // slices, to complete -- before the LDS loads of slice kt + kPfDist are
-  // issued.  The workgroups of an XCD that share a panel split its lines
-  // between them.  Measured: 7% fewer cycles for fp8; none for the 16-bit
-  // kinds, which do not use it.
+  // into LDS, which have about one slice to land.  One dword of every
+  // 128-byte line of slice kt + kPfDist is loaded early (into a scratch LDS
+  // area, no registers), right after the last LDS load that the next
+  // barrier waits for: that barrier waits with vmcnt(1), and the prefetch
+  // has until the barrier after it to complete -- before the LDS loads of
+  // slice kt + kPfDist are issued.  The workgroups of an XCD that share a
+  // panel split its lines between them.  Measured: 7% fewer cycles for fp8
+  // on the scaled 32 x 32 x 64 form, 1.5% on its 16 x 16 x 128 K loop
+  // (which places the prefetch itself); none for the 16-bit kinds, which
+  // do not use it.  (kPfAt: its place in the slices of run_slices.)
   static constexpr int kLastLoad = kFreeAt + (kLoads - 1) * kWindow / kLoads;
   static constexpr bool kPfHead = kLastLoad >= kMfma;  // last load in the next slice's head
   static constexpr int kPfAt = kPfHead ? kLastLoad - kMfma + 1 : kLastLoad + 1;
@@ -449,8 +548,9 @@ struct Kernel {
     return -1;
   }
 
-  // fp6 fragments are 24 bytes: six registers.
-  using Frag = typename std::conditional<T::kFp6, i32x6, typename std::conditional<kW, i32x8, u32x4>::type>::type;
+  // fp8 fragments are 32 bytes, fp6 24 (six registers).
+  using Frag = typename std::conditional<
+      T::kFp6, i32x6, typename std::conditional<T::kDt == kFp8, i32x8, u32x4>::type>::type;
   using Acc = typename std::conditional<kW, f32x16, f32x4>::type;
   struct Frags {
     Frag x[kNBn], y[kNBm];
@@ -468,27 +568,27 @@ struct Kernel {
   typename std::conditional<T::kBK, PanelLoader<kLB>, MNLoader<TN>>::type lb;
   __amdgpu_buffer_rsrc_t pf_rsrc;
   uint32_t pf_off;
-  // Block scales.  Each lane streams the scale bytes of one row per
+  // Block scales.  Each lane takes the scale bytes of one row per
   // "instruction" j (the wave's B rows 64 j .. + 63 for j < 2, its A rows
-  // 64 (j - 2) .. + 63 after) in 16-byte chunks: chunk c is the 16 bytes
-  // from the dword holding the row's first scale byte, plus 16 c.  Any 4
-  // consecutive bytes of the row that start in chunk c can be shifted out
-  // of it and the next chunk's first dword, so two chunks are kept.  A
-  // chunk covers 16 slices of fp8 (one scale per 128 K).  Loading a row's
-  // bytes 16 at a time keeps the texture unit's work small: each of these
-  // loads touches 64 cache lines (one per lane), as many as a 1 KB panel
-  // load touches bytes / 16.  (fp4 and fp6 stage their chunks instead,
-  // below.)
+  // 64 (j - 2) .. + 63 after), addressed from the dword holding the row's
+  // first scale byte.  Any 4 consecutive bytes of the row can be shifted
+  // out of the two dwords from the one holding the first of them.  The
+  // resource ends at the dword holding the tile's last scale byte; the
+  // hardware checks each dword of a load against it (soffset included), so
+  // dwords past it read 0.
   //  * fp8: group g (slices 4 g .. 4 g + 3) is one shifted dword, handed
   //    to the lanes that feed that row to the MFMA; the MFMA's byte select
-  //    then picks the slice.
+  //    then picks the slice.  Each lane loads the group's dword pair itself
+  //    (8 bytes, one load per instruction and group).
+  //  * fp4 and fp6 stage the bytes of every row of the tile in LDS first
+  //    (below).
   // Bytes past the row's last scale block (the next row's, in a padded
   // slice) are zeroed: the slices they would scale hold zeros, and a NaN
   // scale (0xff) would turn those zeros into NaN.
   __amdgpu_buffer_rsrc_t rss[2];  // B scales, A scales; based at the tile's first row, dword aligned
   uint32_t sc_off[4];             // per instruction: aligned byte offset of this lane's row, or kOOB
   uint32_t sc_sh[4];              // per instruction: byte shift of the row inside a dword pair
-  u32x4 sc_ck[4], sc_ckn[4];      // chunks c and c + 1 per instruction (fp6: chunks 2 p and 2 p + 1 of round p)
+  u32x4 sc_ck[4], sc_ckn[4];      // fp6: chunks 2 p and 2 p + 1 of round p per instruction
   // fp4, fp6: the scale chunks of every row of the tile are loaded into LDS
   // once per workgroup (waves 0-1 the B rows, waves 2-3 the A rows), and
   // each wave then reads the rows its MFMAs take (every row feeds two
@@ -537,11 +637,11 @@ struct Kernel {
   u32x4 sv4[4];    // aligned rows: a group on its way from the L2 to its slot
   const LDS_AS uint8_t *sb4;  // aligned rows: the slot of the pair being converted
   // Per block (x blocks, then y blocks): fp8, the bytes of a group of 4
-  // slices, converted into sc_nxt and copied into sc_cur before the group's
-  // first slice.  fp4 and fp6 convert their scales straight into the set
-  // their MFMAs read (fp4: set (kt / 2) % 2 for a pair of slices; fp6: set
-  // (k / 2) % 2 for K step k), so no copy is needed at the start of a slice.
-  int sc_nxt[8], sc_cur[8];
+  // slices, converted into sc_cur block by block between the block's last
+  // MFMA of one group and its first of the next.  fp4 and fp6 convert their
+  // scales into the set their MFMAs read next (fp4: set (kt / 2) % 2 for a
+  // pair of slices; fp6: set (k / 2) % 2 for K step k).
+  int sc_cur[kNR];
   int sc_set[2][kNR];
   Acc acc[kNBn][kNBm];
 
@@ -550,11 +650,13 @@ struct Kernel {
   // Fragment of one block of kBlk rows (B rows = C columns for x, A rows for
   // y), K substep `sub`, from a K-contiguous slot.
   __device__ __forceinline__ Frag read_rows(const LDS_AS uint8_t *slot, int row0, int sub) const {
-    if constexpr (kW) {
-      // 32 x 32 x 64: lane l holds row l % 32 and 32 bytes of K: logical
-      // chunks 4 sub + 2 (l / 32) and the one after.
-      const int c = 4 * sub + 2 * (lane >> 5);
-      const LDS_AS uint8_t *p = slot + (row0 + (lane & 31)) * kRowBytes;
+    if constexpr (T::kDt == kFp8) {
+      // 16 x 16 x 128 on fp8 (one K step per slice): lane l holds row l % 16
+      // and K block l / 16 of the slice, 32 bytes: logical chunks 2 (l / 16)
+      // and the one after.  Each 16-lane row reads 16 rows at one chunk,
+      // which the slot's chunk permutation spreads over all the banks.
+      const int c = 2 * (lane >> 4);
+      const LDS_AS uint8_t *p = slot + (row0 + (lane & 15)) * kRowBytes;
       u32x4 u = *(const LDS_AS u32x4 *)(p + ((c ^ lane_sw) << 4));
       u32x4 v = *(const LDS_AS u32x4 *)(p + (((c + 1) ^ lane_sw) << 4));
       i32x8 r;
@@ -639,10 +741,6 @@ struct Kernel {
       else
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(x), "v"(y));
       return d;
-    } else if constexpr (T::kDt == kFp8) {
-      // Format code 0 (OCP FP8 E4M3) for both operands; byte SEL of each
-      // scale VGPR (the slice's place in its group of 4).
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, SEL, sx, SEL, sy);
     } else if constexpr (T::kFp6) {
       // Format code 2 (OCP FP6 E2M3) or 3 (E3M2): 24 bytes, 32 elements per
       // lane, in the fragment's first six registers; byte SEL of each scale
@@ -652,32 +750,52 @@ struct Kernel {
       const i32x8 y6 = {y[0], y[1], y[2], y[3], y[4], y[5], 0, 0};
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x6, y6, c, F, F, SEL, sx, SEL, sy);
     } else {
-      // Format code 4 (OCP FP4 E2M1) for both operands (cbsz, blgp), 16 x 16
-      // x 128: 16 bytes, 32 elements per lane.  Byte SEL of each scale VGPR:
-      // op_sel bit 0 and op_sel_hi bit 1, the same for both.  Inline asm
-      // with the accumulator tied in place, as for the 16-bit forms.
-#define TGEMM_MFMA4(OPS) "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, " OPS " cbsz:4 blgp:4"
+      // The scaled 16 x 16 x 128 form.  fp4: format code 4 (OCP FP4 E2M1)
+      // for both operands (cbsz, blgp), 16 bytes, 32 elements per lane.
+      // fp8: format code 0 (OCP FP8 E4M3, the default), 32 bytes, 32
+      // elements per lane.  Byte SEL of each scale VGPR: op_sel bit 0 and
+      // op_sel_hi bit 1, the same for both.  Inline asm with the accumulator
+      // tied in place, as for the 16-bit forms.
+#define TGEMM_MFMA_S(SRC_C, OPS) \
+  "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, " SRC_C ", %3, %4 " OPS
+      constexpr bool k4 = T::kDt == kFp4;
       Acc d = c;
       if constexpr (FIRST) {
-        if constexpr (SEL == 0)
-          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[0,0,0] op_sel_hi:[0,0,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        if constexpr (SEL == 0 && k4)
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[0,0,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 1 && k4)
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[1,1,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 2 && k4)
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[0,0,0] op_sel_hi:[1,1,0] cbsz:4 blgp:4") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (k4)
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[1,1,0] op_sel_hi:[1,1,0] cbsz:4 blgp:4") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 0)
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[0,0,0] op_sel_hi:[0,0,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
         else if constexpr (SEL == 1)
-          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[1,1,0] op_sel_hi:[0,0,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
         else if constexpr (SEL == 2)
-          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[0,0,0] op_sel_hi:[1,1,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[0,0,0] op_sel_hi:[1,1,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
         else
-          asm volatile(TGEMM_MFMA4("0, %3, %4 op_sel:[1,1,0] op_sel_hi:[1,1,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+          asm volatile(TGEMM_MFMA_S("0", "op_sel:[1,1,0] op_sel_hi:[1,1,0]") : "=a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
       } else {
-        if constexpr (SEL == 0)
-          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[0,0,0] op_sel_hi:[0,0,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        if constexpr (SEL == 0 && k4)
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[0,0,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 1 && k4)
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[1,1,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 2 && k4)
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[0,0,0] op_sel_hi:[1,1,0] cbsz:4 blgp:4") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (k4)
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[1,1,0] op_sel_hi:[1,1,0] cbsz:4 blgp:4") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+        else if constexpr (SEL == 0)
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[0,0,0] op_sel_hi:[0,0,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
         else if constexpr (SEL == 1)
-          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[1,1,0] op_sel_hi:[0,0,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
         else if constexpr (SEL == 2)
-          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[0,0,0] op_sel_hi:[1,1,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[0,0,0] op_sel_hi:[1,1,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
         else
-          asm volatile(TGEMM_MFMA4("%0, %3, %4 op_sel:[1,1,0] op_sel_hi:[1,1,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
+          asm volatile(TGEMM_MFMA_S("%0", "op_sel:[1,1,0] op_sel_hi:[1,1,0]") : "+a"(d) : "v"(x), "v"(y), "v"(sx), "v"(sy));
       }
-#undef TGEMM_MFMA4
+#undef TGEMM_MFMA_S
       return d;
     }
   }
@@ -798,17 +916,6 @@ struct Kernel {
     const bool ok = kt * kSliceK < kK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (LDS_AS void *)(slots.junk + wave * 256), 4,
                                              ok ? pf_off : kOOB, (uint32_t)kt * T::kSliceBytes, 0, 0);
-  }
-
-  // Chunk c of every instruction's row into dst.  The resource ends at the
-  // dword holding the tile's last scale byte; the hardware checks each dword
-  // of the load against it (soffset included), so dwords past it read 0.
-  __device__ __forceinline__ void load_chunks(u32x4 (&dst)[4], int c) { load_bytes16(dst, 16 * c); }
-  // The 16 bytes from byte b (a multiple of 4) of every instruction's row.
-  __device__ __forceinline__ void load_bytes16(u32x4 (&dst)[4], int b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rss[j >> 1], sc_off[j], (uint32_t)b, 0);
   }
 
   // fp4, fp6: group g (chunks 2 g and 2 g + 1) of this wave's 128 rows into
@@ -1024,25 +1131,34 @@ struct Kernel {
     (pair4_step<0, N, 0>(), ...);
   }
 
-  // fp8: group g, shifted out of the window's first two dwords and
-  // redistributed into sc_nxt: block 2 j + h of instruction j's rows is
-  // rows 32 h .. 32 h + 31, which lane l (both halves of the wave) takes
-  // from lane 32 h + l % 32 (one swap of the wave halves).  The window (chunk, next chunk) then moves on
-  // by one dword; once it has moved a whole chunk the chunk after the next
-  // is loaded, 16 slices ahead of its first use.  (Moving the window keeps
-  // every register index static.)
-  __device__ __forceinline__ void convert_scales(int g) {
-    const uint32_t keep = keep_mask(a.kb - 4 * g);
+  // fp8: the scale bytes of group g (slices 4 g .. 4 g + 3) of each
+  // instruction's row, as the two dwords from the one holding the row's
+  // byte 4 g (one 8-byte load per instruction and group, two slices ahead
+  // of their use; past the resource's end they read 0), shifted out and
+  // handed to the scale registers of the instruction's four blocks.
+  // Instruction J's lane l holds row 64 (J % 2) + l of the wave's x rows (J
+  // < 2) or y rows (rows 64 apart share their shift, as 64 kb is a multiple
+  // of 4); block 4 (J % 2) + c is rows 16 c .. 16 c + 15 of them, which
+  // lane l (every 16-lane row) takes from lane 16 c + l % 16: a swap of the
+  // wave halves (lane l then holds rows 32 h + l % 32 for h = 0, 1), then
+  // of odd and even 16-lane rows of each (rows 32 h + 16 c' + l % 16).
+  u32x2 sc_pr[4];
+  __device__ __forceinline__ void load_pairs8(int g) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t d = __builtin_amdgcn_alignbyte(sc_ck[j][1], sc_ck[j][0], sc_sh[j]) & keep;
-      const auto sw = __builtin_amdgcn_permlane32_swap(d, d, false, false);
-      sc_nxt[2 * j] = (int)sw[0];
-      sc_nxt[2 * j + 1] = (int)sw[1];
-      sc_ck[j] = u32x4{sc_ck[j][1], sc_ck[j][2], sc_ck[j][3], sc_ckn[j][0]};
-      sc_ckn[j] = u32x4{sc_ckn[j][1], sc_ckn[j][2], sc_ckn[j][3], 0u};
-    }
-    if ((g & 3) == 3) load_chunks(sc_ckn, (g >> 2) + 2);
+    for (int j = 0; j < 4; ++j)
+      sc_pr[j] = __builtin_amdgcn_raw_buffer_load_b64(rss[j >> 1], sc_off[j], (uint32_t)(4 * g), 0);
+  }
+  template <int J>
+  __device__ __forceinline__ void convert8(int g) {
+    const uint32_t keep = keep_mask(a.kb - 4 * g);
+    const uint32_t d = __builtin_amdgcn_alignbyte(sc_pr[J][1], sc_pr[J][0], sc_sh[J & 2]) & keep;
+    const auto h = __builtin_amdgcn_permlane32_swap(d, d, false, false);
+    const auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    sc_cur[4 * J] = (int)lo[0];
+    sc_cur[4 * J + 1] = (int)lo[1];
+    sc_cur[4 * J + 2] = (int)hi[0];
+    sc_cur[4 * J + 3] = (int)hi[1];
   }
 
   // MFMA Q (0 .. kMfma - 1) of slice kt held in slot S.  Substep Q / kPerSub;
@@ -1123,8 +1239,6 @@ struct Kernel {
       constexpr int SET4 = (JB >> 1) & 1, SEL4 = 2 * (JB & 1) + SUB;
       acc[I][J] = mma<FIRST && SUB == 0, SEL4>(f.x[I], f.y[J], acc[I][J], sc_set[SET4][I], sc_set[SET4][kNBn + J]);
     }
-    else if constexpr (T::kScaled)
-      acc[I][J] = mma<FIRST && SUB == 0, JB>(f.x[I], f.y[J], acc[I][J], sc_cur[I], sc_cur[4 + J]);
     else
       acc[I][J] = mma<FIRST && SUB == 0>(f.x[I], f.y[J], acc[I][J], 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -1136,14 +1250,9 @@ struct Kernel {
   }
 
   // One K slice kt from slot S (its substep-0 fragments already in f0); JB
-  // = kt % 4 for the block-scaled kinds (fp6: the slot).
+  // = kt % 4 for fp4.
   template <int S, int JB, bool FIRST = false>
   __device__ __forceinline__ void step(int kt, Frags &f0, Frags &f1) {
-    if constexpr (T::kDt == kFp8 && JB == 3) convert_scales((kt + 1) >> 2);
-    if constexpr (T::kDt == kFp8 && JB == 0 && !FIRST) {
-#pragma unroll
-      for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
-    }
     slice_seq<S, JB, FIRST>(std::make_integer_sequence<int, kMfma>(), kt, f0, f1);
   }
 
@@ -1258,8 +1367,8 @@ struct Kernel {
           }
         }
       }
-      if constexpr (T::kDt != kFp4) {
-        // (fp4 starts its accumulators from the MFMA's constant 0.)
+      if constexpr (T::kFp6) {
+        // (fp4 and fp8 start their accumulators from the MFMA's constant 0.)
 #pragma unroll
         for (int i = 0; i < kNBn; ++i)
 #pragma unroll
@@ -1268,12 +1377,14 @@ struct Kernel {
     }
     if constexpr (T::kFp6)
       run6();
+    else if constexpr (T::kDt == kFp8)
+      run8();
     else
       run_slices();
   }
 
-  // The K loop over slices (every kind but fp6), from its prologue to the
-  // epilogue.
+  // The K loop over slices (the 16-bit kinds and fp4), from its prologue to
+  // the epilogue.
   __device__ __forceinline__ void run_slices() {
 
     // Prologue: the first scale chunks, slice 0 into slot 0, the loads of
@@ -1286,9 +1397,6 @@ struct Kernel {
       stage_chunk4(0);
       stage_chunk4(1);
       stage_chunk4(2);
-    } else if constexpr (T::kScaled) {
-      load_chunks(sc_ck, 0);
-      load_chunks(sc_ckn, 1);
     }
     load_slices(std::make_integer_sequence<int, kNS - 1>());
     constexpr int kTailLoads = tail_loads();
@@ -1315,20 +1423,15 @@ struct Kernel {
     }
     if constexpr (kZeroTail)
       if (zt == 0) zero_tail<0>(0);
-    if constexpr (T::kDt == kFp8) {
-      convert_scales(0);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) sc_cur[b] = sc_nxt[b];
-    }
     barrier();
     Frags f0, f1;
     read_all<0>(std::make_integer_sequence<int, kNR>(), f0, 0);
     // Slice 0 starts the accumulators; then the slices go round the ring a
-    // whole number of slots at a time (fp8 and fp4: four, for their scale chunks),
-    // and the one to three left after the last round run on their own, so
-    // no slice past nk is computed.
+    // whole number of slots at a time (fp4: four, for its scale chunks), and
+    // the one to three left after the last round run on their own, so no
+    // slice past nk is computed.
     step<0, 0, true>(0, f0, f1);
-    if constexpr (T::kDt == kFp8 || T::kDt == kFp4) {
+    if constexpr (T::kDt == kFp4) {
       int kt = 1;
       for (; kt + 3 < nk; kt += 4) {
         step<1, 1>(kt, f0, f1);
@@ -1366,6 +1469,169 @@ struct Kernel {
       epilogue_partial(split);
     else
       epilogue();
+  }
+
+  // -------------------------------------------------------------------------
+  // fp8: the scaled 16 x 16 x 128 MFMA.
+  //
+  // A slice (128 bytes of every row, one K step of 128) is 64 MFMAs per
+  // wave, on one set of fragments (16 of 32 bytes: 128 registers; two sets,
+  // as the other kinds keep, do not fit beside the accumulators): each
+  // fragment of the next slice is read into the registers of this slice's
+  // once their last MFMA has issued (the MFMA reads them as it issues; the
+  // LDS data returns later), at the positions f8::schedule gives.  Two
+  // slots: the barrier before MFMA kB8 of slice kt waits for this wave's
+  // loads of slice kt + 1 and publishes them; every read of slot kt % 2 was
+  // issued before it (the last in the head of slice kt), so the loads of
+  // slice kt + 2 go into that slot from there on, one every two MFMAs, and
+  // the L2 prefetch of slice kt + 3 after the last of them.  The scales of
+  // group g (slices 4 g .. 4 g + 3) are loaded in slice 4 g - 3 and
+  // converted in slices 4 g - 1 and 4 g (kCv8).  Measured at 4096^3 against
+  // the scaled 32 x 32 x 64 form: 2-3% less time (5% higher clock under
+  // the power limit, 3% more cycles: 2.5% more issue cycles per flop, and
+  // reads that wait for their slot in the busier LDS); the barrier at 16,
+  // 24 or 32, and the y blocks in x-block pairs rather than quadrants,
+  // within 1% of each other.
+  static constexpr int kB8 = 24;
+  static constexpr f8::Sched kSch8[2] = {f8::schedule(0, kB8), f8::schedule(1, kB8)};
+  // Position of the conversion of instruction J's scales (blocks 4 J ..
+  // 4 J + 3: x blocks for J < 2, y blocks after) in slice 4 g - 1 (phase
+  // 1), or in slice 4 g (phase 0) at kM and on.
+  static constexpr int kCv8[4] = {33, f8::kM + 5, 56, f8::kM + 3};
+
+  // Load instruction i (A panel for i < kLA, then B) of slice kt into slot
+  // S, as PanelLoader::issue / issue_masked, with the lane's offset rebuilt
+  // from one of two bases (instructions i and i + 2 are 16 rows apart)
+  // rather than held per instruction: 12 registers fewer, which the fp8
+  // kernel needs.  A row past the panel's last needs no out-of-range
+  // offset: it starts at least ld >= K bytes past the start of the last
+  // row, at or past the end of the resource.
+  uint32_t lo8[2][2];  // [B][parity]: this lane's chunk offset at slice 0 in instruction 0 / 1
+  int kcol8[2];        // element column of this lane's chunk inside a slice (parity)
+  template <int S>
+  __device__ __forceinline__ void load8(int kt, int i) {
+    const bool isb = i >= kLA;
+    const int ii = isb ? i - kLA : i;
+    const uint32_t ld = (uint32_t)(isb ? a.ldb : a.lda);
+    uint32_t v = lo8[isb][ii & 1] + (uint32_t)(ii >> 1) * 16u * ld;
+    if constexpr (!T::kWholeK) v = kt * kSliceK + kcol8[ii & 1] < kK ? v : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isb ? lb.rsrc : la.rsrc,
+                                             (LDS_AS void *)((isb ? slots.b[S] : slots.a[S]) + (wave * kLA + ii) * 1024),
+                                             16, v, (uint32_t)kt * T::kSliceBytes, 0, 0);
+  }
+
+  // Fragment F (x blocks, then y blocks) of the slice in slot S.
+  template <int S, int F>
+  __device__ __forceinline__ void read8(Frags &f) const {
+    if constexpr (F < kNBn)
+      f.x[F] = read_rows(slots.b[S], wave_n * kWN + F * kBlk, 0);
+    else
+      f.y[F - kNBn] = read_rows(slots.a[S], wave_m * kWM + (F - kNBn) * kBlk, 0);
+  }
+  // The reads at MFMA Q of a slice of phase P in slot S: the next slice's
+  // fragments placed here, and this slice's placed at kM + Q by the
+  // previous slice (none in the first slice, whose fragments the prologue
+  // reads).
+  template <int S, int P, int Q, bool FIRST, int F>
+  __device__ __forceinline__ void read8_at(Frags &f) const {
+    if constexpr (kSch8[P].pos[F] == Q) read8<S ^ 1, F>(f);
+    if constexpr (!FIRST && kSch8[P ^ 1].pos[F] == f8::kM + Q) read8<S, F>(f);
+  }
+  template <int S, int P, int Q, bool FIRST, int... F>
+  __device__ __forceinline__ void reads8(std::integer_sequence<int, F...>, Frags &f) const {
+    (read8_at<S, P, Q, FIRST, F>(f), ...);
+  }
+
+  // MFMA Q of slice kt (JB = kt % 4; slot and phase kt % 2).
+  template <int JB, bool FIRST, int Q>
+  __device__ __forceinline__ void mfma8(int kt, Frags &f) {
+    constexpr int S = JB & 1;
+    if constexpr (Q == kB8) {
+      wait_vm_lgkm0<(kPfDist > 0 ? 1 : 0)>();
+      barrier();
+      // Slice 4 g + 1 loads the scales of group g + 1 (the next barrier
+      // waits for them).
+      if constexpr (JB == 1) load_pairs8((kt + 3) >> 2);
+    }
+    // The scales of group g go into the registers of each block once its
+    // last MFMA of slice 4 g - 1 has issued, and at least two MFMAs before
+    // its first of slice 4 g (the wait states between a VALU write and an
+    // MFMA that reads the register, which the compiler does not place for
+    // an inline-asm MFMA).
+    if constexpr (JB == 3 && Q == kCv8[0]) convert8<0>((kt + 1) >> 2);
+    if constexpr (JB == 3 && Q == kCv8[2]) convert8<2>((kt + 1) >> 2);
+    if constexpr (JB == 0 && !FIRST && Q == kCv8[1] - f8::kM) convert8<1>(kt >> 2);
+    if constexpr (JB == 0 && !FIRST && Q == kCv8[3] - f8::kM) convert8<3>(kt >> 2);
+    reads8<S, S, Q, FIRST>(std::make_integer_sequence<int, 2 * f8::kNB>(), f);
+    if constexpr (Q >= kB8 && (Q - kB8) % 2 == 0 && (Q - kB8) / 2 < kLoads) load8<S>(kt + 2, (Q - kB8) / 2);
+    if constexpr (kPfDist > 0 && Q == f8::kM - 1) prefetch(kt + kPfDist);
+    constexpr f8::IJ o = f8::order(S, Q);
+    acc[o.i][o.j] = mma<FIRST, JB>(f.x[o.i], f.y[o.j], acc[o.i][o.j], sc_cur[o.i], sc_cur[kNBn + o.j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <int JB, bool FIRST, int... Q>
+  __device__ __forceinline__ void slice8(std::integer_sequence<int, Q...>, int kt, Frags &f) {
+    (mfma8<JB, FIRST, Q>(kt, f), ...);
+  }
+  template <int JB, bool FIRST = false>
+  __device__ __forceinline__ void step8(int kt, Frags &f) {
+    // (Without this the compiler computes the 16 load offsets ahead of the
+    // loop and holds them in registers, which made it spill.)
+    asm volatile("" : "+v"(lo8[0][0]), "+v"(lo8[0][1]), "+v"(lo8[1][0]), "+v"(lo8[1][1]));
+    slice8<JB, FIRST>(std::make_integer_sequence<int, f8::kM>(), kt, f);
+  }
+  template <int... F>
+  __device__ __forceinline__ void read8_all(std::integer_sequence<int, F...>, Frags &f) const {
+    (read8<0, F>(f), ...);
+  }
+
+  __device__ __forceinline__ void run8() {
+    static_assert(TM == 256 && TN == 256 && kNBn == f8::kNB && kNBm == f8::kNB && kNS == 2,
+                  "fp8: 256 x 256 tiles, 16 x 16 blocks, two slots");
+    static_assert(f8::schedule_ok(kB8), "fp8 fragment reads");
+    static_assert(f8::convert_ok(kCv8[0], 0) && f8::convert_ok(kCv8[1], 1) && f8::convert_ok(kCv8[2], 2) &&
+                      f8::convert_ok(kCv8[3], 3) && kCv8[0] > kB8 && kCv8[2] > kB8,
+                  "fp8 scale conversions");
+    static_assert(kB8 + 2 * (kLoads - 1) < f8::kM - 1, "fp8 loads: one every two MFMAs from the barrier");
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      kcol8[par] = ((lane & 7) ^ swz(8 * par + (lane >> 3))) * 16;
+      const uint32_t r = (uint32_t)(wave * 8 * kLA + 8 * par + (lane >> 3));
+      lo8[0][par] = r * (uint32_t)a.lda + (uint32_t)kcol8[par];
+      lo8[1][par] = r * (uint32_t)a.ldb + (uint32_t)kcol8[par];
+    }
+    // Prologue: the scales of group 0, slices 0 and 1 into their slots, the
+    // L2 prefetch of slice 2; wait for all but slice 1 and the prefetch.
+    load_pairs8(0);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load8<0>(0, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load8<1>(1, i);
+    if constexpr (kPfDist > 0) prefetch(2);
+    wait_vm_lgkm0<(kLoads + (kPfDist > 0 ? 1 : 0))>();
+    convert8<0>(0);
+    convert8<1>(0);
+    convert8<2>(0);
+    convert8<3>(0);
+    barrier();
+    Frags f;
+    read8_all(std::make_integer_sequence<int, 2 * f8::kNB>(), f);
+    // Slice 0 starts the accumulators; then rounds of four slices (a scale
+    // group), and the one to three left run on their own.
+    step8<0, true>(0, f);
+    int kt = 1;
+    for (; kt + 3 < nk; kt += 4) {
+      step8<1>(kt, f);
+      step8<2>(kt + 1, f);
+      step8<3>(kt + 2, f);
+      step8<0>(kt + 3, f);
+    }
+    if (kt < nk) step8<1>(kt, f);
+    if (kt + 1 < nk) step8<2>(kt + 1, f);
+    if (kt + 2 < nk) step8<3>(kt + 2, f);
+    wait_vm_lgkm0<0>();
+    fence_acc();
+    epilogue();
   }
 
   // -------------------------------------------------------------------------
