@@ -653,12 +653,13 @@ struct Kernel {
     if constexpr (T::kDt == kFp8) {
       // 16 x 16 x 128 on fp8 (one K step per slice): lane l holds row l % 16
       // and K block l / 16 of the slice, 32 bytes: logical chunks 2 (l / 16)
-      // and the one after.  Each 16-lane row reads 16 rows at one chunk,
-      // which the slot's chunk permutation spreads over all the banks.
-      const int c = 2 * (lane >> 4);
+      // and the one after, which the fp8 slots keep at chunks l / 16 and
+      // l / 16 + 4 (before the row's permutation; chunk8_of), so that each
+      // read has the 16-bit kinds' conflict-free pattern.
+      const int g = lane >> 4;
       const LDS_AS uint8_t *p = slot + (row0 + (lane & 15)) * kRowBytes;
-      u32x4 u = *(const LDS_AS u32x4 *)(p + ((c ^ lane_sw) << 4));
-      u32x4 v = *(const LDS_AS u32x4 *)(p + (((c + 1) ^ lane_sw) << 4));
+      u32x4 u = *(const LDS_AS u32x4 *)(p + ((g ^ lane_sw) << 4));
+      u32x4 v = *(const LDS_AS u32x4 *)(p + (((g + 4) ^ lane_sw) << 4));
       i32x8 r;
       r[0] = u[0]; r[1] = u[1]; r[2] = u[2]; r[3] = u[3];
       r[4] = v[0]; r[5] = v[1]; r[6] = v[2]; r[7] = v[3];
@@ -1506,6 +1507,11 @@ struct Kernel {
   // kernel needs.  A row past the panel's last needs no out-of-range
   // offset: it starts at least ld >= K bytes past the start of the last
   // row, at or past the end of the resource.
+  // fp8 slots keep logical chunk 2 g + h of a row at chunk g + 4 h (then
+  // permuted by the row like the other kinds'): this is the logical chunk
+  // at chunk q.  (With the logical order the fragment reads met 2-way bank
+  // conflicts: every read took twice its cycles.)
+  __device__ static __forceinline__ int chunk8_of(int q) { return ((q & 3) << 1) | (q >> 2); }
   uint32_t lo8[2][2];  // [B][parity]: this lane's chunk offset at slice 0 in instruction 0 / 1
   int kcol8[2];        // element column of this lane's chunk inside a slice (parity)
   template <int S>
@@ -1595,7 +1601,7 @@ struct Kernel {
     static_assert(kB8 + 2 * (kLoads - 1) < f8::kM - 1, "fp8 loads: one every two MFMAs from the barrier");
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      kcol8[par] = ((lane & 7) ^ swz(8 * par + (lane >> 3))) * 16;
+      kcol8[par] = chunk8_of((lane & 7) ^ swz(8 * par + (lane >> 3))) * 16;
       const uint32_t r = (uint32_t)(wave * 8 * kLA + 8 * par + (lane >> 3));
       lo8[0][par] = r * (uint32_t)a.lda + (uint32_t)kcol8[par];
       lo8[1][par] = r * (uint32_t)a.ldb + (uint32_t)kcol8[par];
