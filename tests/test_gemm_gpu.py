@@ -227,6 +227,24 @@ def test_mxfp8_per_row_and_per_block_scales_bitwise():
     assert_bitwise(to_bits(run("mxfp8_nt", x, M, N, K)), oracle_full("mxfp8_nt", x), "mxfp8 scales")
 
 
+@pytest.mark.parametrize("slices", [1, 2, 3, 5, 6, 7, 9, 33])
+def test_mxfp8_slice_counts_bitwise(slices):
+    """K a whole number of 128-element slices (the kernel that checks no
+    columns), every count of slices left after the K loop's rounds of four
+    (each slice's fragments are read during the one before, each group of
+    four slices' scales during the group before), several tiles with a
+    ragged N, a different power-of-two scale per row and block: integer
+    elements and scales within 2^-2 .. 2^2 keep every fp32 sum exact, so the
+    result is compared bit for bit."""
+    M, N, K = 264, 520, 128 * slices
+    x = workloads.make_integer("mxfp8_nt", M, N, K, seed=70 + slices)
+    rng = np.random.default_rng(slices)
+    x["sA"] = rng.integers(125, 130, x["sA"].shape).astype(np.uint8)
+    x["sB"] = rng.integers(125, 130, x["sB"].shape).astype(np.uint8)
+    print(f"[gpu] mxfp8_nt slices={slices} M={M} N={N} K={K}", flush=True)
+    assert_bitwise(to_bits(run("mxfp8_nt", x, M, N, K)), oracle_full("mxfp8_nt", x), f"mxfp8 {slices} slices")
+
+
 @pytest.mark.parametrize("offset", [1, 2, 3])
 def test_mxfp8_unaligned_scale_pointers(offset):
     """The scale arrays need no alignment: views starting 1-3 bytes into a
