@@ -400,7 +400,7 @@ constexpr int first_use(int p, int F) {
 // (before MFMA pos of this slice; kM and on: of the next slice): each
 // fragment once its registers are free (after its last MFMA here) and the
 // barrier before MFMA `bar` has published the next slice, in order of
-// availability, at least `gap` MFMAs apart (a fragment is two 16-byte LDS
+// availability, at least kGap MFMAs apart (a fragment is two 16-byte LDS
 // reads per lane; the LDS also takes the loads of the slice after).
 struct Sched {
   int pos[2 * kNB];
