@@ -1488,11 +1488,11 @@ struct Kernel {
   // the L2 prefetch of slice kt + 3 after the last of them.  The scales of
   // group g (slices 4 g .. 4 g + 3) are loaded in slice 4 g - 3 and
   // converted in slices 4 g - 1 and 4 g (kCv8).  Measured at 4096^3 against
-  // the scaled 32 x 32 x 64 form: 2-3% less time (5% higher clock under
-  // the power limit, 3% more cycles: 2.5% more issue cycles per flop, and
-  // reads that wait for their slot in the busier LDS); the barrier at 16,
-  // 24 or 32, and the y blocks in x-block pairs rather than quadrants,
-  // within 1% of each other.
+  // the scaled 32 x 32 x 64 form: 2-4% less time (a 6% higher clock under
+  // the power limit at 2% more cycles, mostly the form's issue: 32.8
+  // cycles per MFMA against 32.1 for half a 32 x 32 x 64 one).  The
+  // barrier at 16 or 32, the loads further apart, or the y blocks in x-block
+  // pairs rather than quadrants measured no better.
   static constexpr int kB8 = 24;
   static constexpr f8::Sched kSch8[2] = {f8::schedule(0, kB8), f8::schedule(1, kB8)};
   // Position of the conversion of instruction J's scales (blocks 4 J ..
